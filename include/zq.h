@@ -1,0 +1,180 @@
+/*
+ * zq.h -- C-ABI of libzq.so: weight-only quantized linear layers on AMD MI355X
+ * (gfx950, CDNA4).
+ *
+ * The operation: Y[M][N] = X[M][K] * dequant(Wq)[N][K]^T, with fp16 or bf16
+ * activations X, packed signed integer weight codes Wq dequantized on the fly,
+ * and fp32 accumulation.
+ *
+ * Sources, cited by page title and section (all are web pages about the ZSE
+ * inference engine):
+ *   [wiki]  the wiki.iphoster.net article "ZSE - open-source движок для запуска
+ *           LLM локально на GPU - 2026"
+ *   [ocr]   the openclawradar.com articles "ZSE: Motor de inferência de LLM de
+ *           código aberto ..." (pt) and "ZSE: Open-Source-LLM-Inferenz-Engine
+ *           ..." (de)
+ *   [lavx]  the news.lavx.hu article "ZSE: A Memory-Efficient LLM Inference
+ *           Engine with Smart Resource Orchestration"
+ *
+ * ---------------------------------------------------------------------------
+ * Packed weight format (fixed by this library)
+ *   [wiki, section "Формат модели .zse"] quantizes groups of 128 weights, packs
+ *   two 4-bit values per byte with the low nibble first, keeps fp16 scales and
+ *   quantizes at conversion time rather than at load time. [ocr, section
+ *   "Componentes da arquitetura"; lavx, section "Technical Architecture"]
+ *   describe zQuantize as per-tensor INT2..INT8 mixed precision. This library
+ *   keeps the group size, the nibble order and the fp16 scales, and uses
+ *   symmetric signed codes (no zero point):
+ *   - bits b in {2, 4, 8}; codes q are two's complement in [-2^(b-1), 2^(b-1)-1];
+ *   - codes run along K; 8/b codes per byte; code i of a byte sits in bits
+ *     [b*i + b-1 : b*i] (INT4: even k in the low nibble); rows are dense,
+ *     row r starts at byte r * k*b/8; no padding;
+ *   - scales are IEEE binary16 bit patterns: group = 0 -> one scale for the
+ *     whole tensor; group = 128 -> one per row and per 128 consecutive k,
+ *     laid out [n][k/128] row-major;
+ *   - w_deq[n][k] = q[n][k] * scale(n, k).
+ *
+ * Conventions for every call
+ *   - Pointers named "device" are device memory owned by the caller (for
+ *     example a torch tensor's data_ptr()). The library never frees or keeps
+ *     them. zq_gemv / zq_gemm / zq_unpack allocate nothing.
+ *   - `stream` is a hipStream_t (NULL = the null stream). gemv, gemm and
+ *     unpack only enqueue work on it and return; faults inside a kernel
+ *     surface at the caller's next synchronisation, as for any HIP kernel.
+ *   - Every argument is validated before any HIP call. A failed check returns
+ *     ZQ_ERR_INVALID_ARG (null pointer, negative size, leading dimension too
+ *     small, dtype not accepted by the call) or ZQ_ERR_UNSUPPORTED (bits not
+ *     in {2,4,8}, group not in {0,128}, k not a multiple of the group or of
+ *     8/bits); nothing is launched and nothing aborts. ZQ_ERR_HIP reports a
+ *     failed HIP runtime call. zq_last_error() then holds a one-line detail
+ *     for the calling thread.
+ *   - Fast paths want 16-byte aligned pointers and rows whose byte length is a
+ *     multiple of 16; any other legal shape runs on a slower general kernel
+ *     with the same results.
+ *   - Sizes are element counts (int64_t). n == 0, k == 0 or m == 0 is legal
+ *     and does nothing (k == 0 with n > 0 writes zeros).
+ * ---------------------------------------------------------------------------
+ */
+#ifndef ZQ_H
+#define ZQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ZQ_OK = 0,
+  ZQ_ERR_INVALID_ARG = 1,
+  ZQ_ERR_UNSUPPORTED = 2,
+  ZQ_ERR_RANGE = 3,  /* non-finite input, scale beyond fp16, code out of range */
+  ZQ_ERR_HIP = 4
+} zq_status;
+
+typedef enum {
+  ZQ_I8 = 0,   /* int8 integer codes */
+  ZQ_F16 = 1,  /* IEEE binary16 */
+  ZQ_BF16 = 2, /* bfloat16 */
+  ZQ_F32 = 3   /* IEEE binary32 */
+} zq_dtype;
+
+/* A packed weight matrix resident in device memory (nn.Linear layout [n][k]). */
+typedef struct zq_weight {
+  int32_t bits;           /* 2, 4 or 8 */
+  int32_t group;          /* 0: one scale per tensor; 128: per row and 128 k */
+  int64_t n;              /* output features (rows) */
+  int64_t k;              /* input features */
+  const void* packed;     /* device, zq_packed_bytes(bits, n, k) bytes */
+  const uint16_t* scales; /* device, zq_num_scales(group, n, k) fp16 patterns */
+} zq_weight;
+
+/* Bytes of packed codes: n * k * bits / 8. Returns 0 for unsupported bits. */
+size_t zq_packed_bytes(int bits, int64_t n, int64_t k);
+
+/* Number of fp16 scales: 1 for group 0, n * (k / 128) for group 128;
+ * -1 for an unsupported group. */
+int64_t zq_num_scales(int group, int64_t n, int64_t k);
+
+/*
+ * zq_pack -- quantize (when given floats) and pack one weight matrix.
+ * [wiki, section "Формат модели .zse": quantization happens once, when a
+ * model is converted; groups of 128; two INT4 per byte, low nibble first.]
+ *
+ *   w          device, [n][k] row-major, dtype w_dtype:
+ *              ZQ_I8  -- ready-made integer codes: pure bit packing. Codes
+ *                        outside [-2^(b-1), 2^(b-1)-1] give ZQ_ERR_RANGE.
+ *                        scales_in, if non-NULL, is copied to scales_out.
+ *              ZQ_F16 / ZQ_BF16 / ZQ_F32 -- float weights to quantize.
+ *   scales_in  device, NULL or zq_num_scales fp16 patterns fixed by the
+ *              caller. NULL with float weights: scales are computed per unit
+ *              (the tensor, or 128 k of one row) as
+ *                a = max|w|; a == 0 -> scale +0;
+ *                else s = fp16_round_nearest_even(a / qmax), qmax = 2^(b-1)-1,
+ *                raised to the next fp16 when s * qmax < a (so no code clips);
+ *              given scales are used as they are and codes clip.
+ *   codes      q = clamp(round_half_even(w / s), -2^(b-1), 2^(b-1)-1), the
+ *              division in double; s == 0 gives q = 0.
+ *   packed_out device, zq_packed_bytes(bits, n, k) bytes, written.
+ *   scales_out device, zq_num_scales fp16 patterns, written (may be NULL only
+ *              when w_dtype is ZQ_I8 or when scales_in is given).
+ * Synchronous: returns after the work on `stream` has finished.
+ * ZQ_ERR_RANGE for a non-finite weight or scale, or a scale beyond the fp16
+ * range; packed_out / scales_out contents are then unspecified. It allocates
+ * and frees a few bytes of device memory for the error flag.
+ */
+zq_status zq_pack(const void* w, zq_dtype w_dtype, int64_t n, int64_t k, int bits,
+                  int group, const uint16_t* scales_in, void* packed_out,
+                  uint16_t* scales_out, void* stream);
+
+/*
+ * zq_unpack -- decode a packed matrix. [wiki, section "Компилятор GPU-ядер":
+ * the unpack_int4 intrinsic; this is its signed form for 2, 4 and 8 bits.]
+ *   out  device, [n][k] row-major of out_dtype:
+ *        ZQ_I8  -- the integer codes, sign-extended;
+ *        ZQ_F32 -- q * s exactly;
+ *        ZQ_F16 / ZQ_BF16 -- q * s rounded to nearest even.
+ * Asynchronous on `stream`.
+ */
+zq_status zq_unpack(const zq_weight* W, void* out, zq_dtype out_dtype, void* stream);
+
+/*
+ * zq_gemv -- decode step, one activation row: y[n] = sum_k x[k] * w_deq[n][k].
+ * [wiki, section "Оркестратор и GPU-ядра": a hand-written wave-64 INT4 GEMV
+ * with 128-bit weight loads is the main small-batch kernel on AMD; section
+ * "Компилятор GPU-ядер": dequantizing matmuls are hand-written kernels.]
+ *   W       packed weight (device pointers inside).
+ *   x       device, k elements of x_dtype (ZQ_F16 or ZQ_BF16).
+ *   y       device, n elements of y_dtype (ZQ_F32, ZQ_F16 or ZQ_BF16); the fp32
+ *           sums are rounded to nearest even for F16 / BF16.
+ * Asynchronous on `stream`. Same result as zq_gemm with m = 1.
+ */
+zq_status zq_gemv(const zq_weight* W, const void* x, zq_dtype x_dtype, void* y,
+                  zq_dtype y_dtype, void* stream);
+
+/*
+ * zq_gemm -- batched decode and prefill: Y[m][n] = sum_k X[m][k] * w_deq[n][k].
+ * [wiki, sections "Оркестратор и GPU-ядра" (small batches) and "Честные
+ * ограничения" / "Перспективы" (concurrent INT4 decode at batch 4..16).]
+ *   X       device, m rows of k elements, row stride ldx >= k elements,
+ *           dtype ZQ_F16 or ZQ_BF16.
+ *   Y       device, m rows of n elements, row stride ldy >= n, dtype ZQ_F32,
+ *           ZQ_F16 or ZQ_BF16.
+ * Small m runs on a vector-ALU kernel; larger m dequantizes weight tiles to
+ * bf16 / fp16 (exact for every code) and runs the contraction on MFMA.
+ * Asynchronous on `stream`.
+ */
+zq_status zq_gemm(const zq_weight* W, const void* X, zq_dtype x_dtype, int64_t m,
+                  int64_t ldx, void* Y, zq_dtype y_dtype, int64_t ldy, void* stream);
+
+/* Static description of a status code. */
+const char* zq_status_string(zq_status s);
+
+/* Detail of the last failed call made by this thread ("" if none). */
+const char* zq_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ZQ_H */

@@ -1,0 +1,62 @@
+// zq_internal.hpp -- host-side interfaces between the C-ABI layer (zq_api.hip)
+// and the kernel launchers of libzq.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace zq {
+
+struct DeviceInfo {
+  int device = -1;
+  int num_cus = 0;
+  int num_xcds = 8;
+};
+// Properties of the current device, queried once per device and cached.
+const DeviceInfo& device_info();
+
+// One validated problem Y[m][n] = X[m][k] * dequant(W)^T, all device pointers.
+struct GemmArgs {
+  const uint8_t* packed;
+  const uint16_t* scales;
+  int bits, group;
+  int64_t n, k;
+  const uint16_t* x;
+  int xt;  // XF16 / XBF16
+  int64_t m, ldx;
+  void* y;
+  int yt;  // YF32 / YF16 / YBF16
+  int64_t ldy;
+  hipStream_t stream;
+};
+
+// vector-ALU kernel for m <= 4 with x staged in LDS
+size_t gemv_valu_lds_bytes(int bits, int64_t m, int64_t k);
+hipError_t launch_gemv_valu(const GemmArgs& a);
+// MFMA kernels for larger m
+bool gemm_mfma_supported(const GemmArgs& a);
+hipError_t launch_gemm_mfma(const GemmArgs& a);
+// general kernel: any legal shape and alignment
+hipError_t launch_gemm_general(const GemmArgs& a);
+// Y rows of n zeros (a fill kernel, so it is safe under stream capture)
+hipError_t launch_zero_rows(void* y, int esz, int64_t m, int64_t n, int64_t ldy, hipStream_t s);
+
+// pack / unpack
+struct PackArgs {
+  const void* w;
+  int wt;  // 0 = int8 codes, 1 = f16, 2 = bf16, 3 = f32
+  int64_t n, k;
+  int bits, group;
+  const uint16_t* scales;  // scales used for quantizing (given or computed)
+  uint8_t* packed;
+  uint32_t* flags;         // device: [0] error bits, [1] absmax bits
+  hipStream_t stream;
+};
+enum : uint32_t { FLAG_NONFINITE = 1u, FLAG_SCALE_RANGE = 2u, FLAG_CODE_RANGE = 4u };
+hipError_t launch_compute_scales(const PackArgs& a, uint16_t* scales_out);
+hipError_t launch_quantize_pack(const PackArgs& a);
+hipError_t launch_unpack(const uint8_t* packed, const uint16_t* scales, int bits, int group,
+                         int64_t n, int64_t k, void* out, int out_dtype, hipStream_t stream);
+
+}  // namespace zq

@@ -1,0 +1,158 @@
+"""Thin ctypes binding of libzq.so (C-ABI in include/zq.h).
+
+Argument marshalling only: every step runs in the HIP kernels of libzq. Tensors
+must live on a ROCm device; calls enqueue on torch's current stream. There is
+no CPU path: if the library is missing, every call raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libzq.so")
+
+OK, ERR_INVALID_ARG, ERR_UNSUPPORTED, ERR_RANGE, ERR_HIP = 0, 1, 2, 3, 4
+I8, F16, BF16, F32 = 0, 1, 2, 3
+_DT = {torch.int8: I8, torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
+
+# every exported symbol of include/zq.h
+SYMBOLS = ("zq_packed_bytes", "zq_num_scales", "zq_pack", "zq_unpack", "zq_gemv", "zq_gemm",
+           "zq_status_string", "zq_last_error")
+
+
+class ZqError(RuntimeError):
+    def __init__(self, status: int, call: str, detail: str):
+        super().__init__(f"{call}: status {status} ({detail})")
+        self.status = status
+
+
+class _Weight(ctypes.Structure):
+    _fields_ = [("bits", ctypes.c_int32), ("group", ctypes.c_int32), ("n", ctypes.c_int64),
+                ("k", ctypes.c_int64), ("packed", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libzq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m weight_quantized_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        wp = ctypes.POINTER(_Weight)
+        L.zq_packed_bytes.argtypes = [i32, i64, i64]
+        L.zq_packed_bytes.restype = ctypes.c_size_t
+        L.zq_num_scales.argtypes = [i32, i64, i64]
+        L.zq_num_scales.restype = i64
+        L.zq_pack.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp, vp, vp]
+        L.zq_unpack.argtypes = [wp, vp, i32, vp]
+        L.zq_gemv.argtypes = [wp, vp, i32, vp, i32, vp]
+        L.zq_gemm.argtypes = [wp, vp, i32, i64, i64, vp, i32, i64, vp]
+        for f in ("zq_pack", "zq_unpack", "zq_gemv", "zq_gemm"):
+            getattr(L, f).restype = i32
+        L.zq_status_string.argtypes = [i32]
+        L.zq_status_string.restype = ctypes.c_char_p
+        L.zq_last_error.argtypes = []
+        L.zq_last_error.restype = ctypes.c_char_p
+        _lib = L
+    return _lib
+
+
+def _check(status: int, call: str) -> None:
+    if status != OK:
+        raise ZqError(status, call, lib().zq_last_error().decode())
+
+
+def _stream(t: torch.Tensor) -> int:
+    return torch.cuda.current_stream(t.device).cuda_stream
+
+
+def _ptr(t: torch.Tensor | None) -> int | None:
+    return None if t is None else t.data_ptr()
+
+
+def packed_bytes(bits: int, n: int, k: int) -> int:
+    return lib().zq_packed_bytes(bits, n, k)
+
+
+def num_scales(group: int, n: int, k: int) -> int:
+    return lib().zq_num_scales(group, n, k)
+
+
+@dataclass
+class ZqWeight:
+    """A packed weight matrix in device memory: codes [n][k*bits/8] uint8 and fp16 scales."""
+    bits: int
+    group: int
+    n: int
+    k: int
+    packed: torch.Tensor
+    scales: torch.Tensor
+
+    def desc(self) -> _Weight:
+        return _Weight(self.bits, self.group, self.n, self.k, _ptr(self.packed), _ptr(self.scales))
+
+    @property
+    def nbytes(self) -> int:
+        return self.packed.numel() + 2 * self.scales.numel()
+
+
+def pack(w: torch.Tensor, bits: int, group: int, scales: torch.Tensor | None = None) -> ZqWeight:
+    """Quantize (float w) or bit-pack (int8 codes) an [n][k] device tensor. Synchronous."""
+    n, k = w.shape
+    w = w.contiguous()
+    nb = packed_bytes(bits, n, k)
+    ns = num_scales(group, n, k)
+    packed = torch.empty(max(nb, 0), dtype=torch.uint8, device=w.device)
+    out_scales = torch.empty(max(ns, 1), dtype=torch.float16, device=w.device)
+    sin = None if scales is None else scales.contiguous()
+    _check(lib().zq_pack(_ptr(w), _DT.get(w.dtype, -1), n, k, bits, group, _ptr(sin), _ptr(packed),
+                         _ptr(out_scales), _stream(w)), "zq_pack")
+    return ZqWeight(bits, group, n, k, packed, out_scales)
+
+
+def unpack(W: ZqWeight, dtype: torch.dtype = torch.int8) -> torch.Tensor:
+    out = torch.empty((W.n, W.k), dtype=dtype, device=W.packed.device)
+    d = W.desc()
+    _check(lib().zq_unpack(ctypes.byref(d), _ptr(out), _DT.get(dtype, -1), _stream(out)), "zq_unpack")
+    return out
+
+
+def gemv(W: ZqWeight, x: torch.Tensor, out: torch.Tensor | None = None,
+         out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """y[n] = sum_k x[k] * w_deq[n][k] for one activation row x [k]."""
+    if out is None:
+        out = torch.empty(W.n, dtype=out_dtype, device=x.device)
+    d = W.desc()
+    _check(lib().zq_gemv(ctypes.byref(d), _ptr(x), _DT.get(x.dtype, -1), _ptr(out),
+                         _DT.get(out.dtype, -1), _stream(x)), "zq_gemv")
+    return out
+
+
+def gemm(W: ZqWeight, X: torch.Tensor, out: torch.Tensor | None = None,
+         out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
+    """Y[m][n] = sum_k X[m][k] * w_deq[n][k]; X may have a row stride >= k."""
+    m = X.shape[0]
+    assert X.dim() == 2 and X.stride(1) == 1
+    if out is None:
+        out = torch.empty((m, W.n), dtype=out_dtype, device=X.device)
+    assert out.dim() == 2 and out.stride(1) == 1
+    d = W.desc()
+    _check(lib().zq_gemm(ctypes.byref(d), _ptr(X), _DT.get(X.dtype, -1), m, X.stride(0), _ptr(out),
+                         _DT.get(out.dtype, -1), out.stride(0), _stream(X)), "zq_gemm")
+    return out
+
+
+def gemm_raw(W: ZqWeight, x_ptr: int, x_dtype: int, m: int, ldx: int, y_ptr: int, y_dtype: int,
+             ldy: int, stream: int) -> None:
+    """zq_gemm on raw device pointers (benchmark loops: no tensor bookkeeping)."""
+    d = W.desc()
+    _check(lib().zq_gemm(ctypes.byref(d), x_ptr, x_dtype, m, ldx, y_ptr, y_dtype, ldy, stream),
+           "zq_gemm")
