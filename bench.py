@@ -1,0 +1,261 @@
+#!/usr/bin/env python3
+"""Throughput of the weight-only quantized linear layer on one MI355X.
+
+Default workload (one "step" = one decode token through a Qwen2.5-7B-shaped
+stack): 28 layers x 7 projections (q, k, v, o, gate, up, down), each its own
+INT4 group-128 weight, M = 1, fp16 activations, fp32 outputs; 196 launches of
+zq_gemm per step, replayed as one HIP graph. All inputs are synthetic, seeded
+and resident in HBM before timing starts.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--config qwen7b-decode]
+
+Prints one JSON line. Other workloads (--config):
+  gemv-512             single 512 x 512 INT4 GEMV, per-tensor scale fp16(0.02)
+  qwen7b-batch --m M   the 7B stack at M in {1,4,8,16,32}, bf16 activations
+  qwen32b-decode       64 layers of Qwen2.5-32B projection shapes, M = 1
+  qwen7b-prefill       7B stack, bits per layer from {2,4,8}, per-tensor scales,
+                       M = 2048 bf16 tokens (MFMA-bound: TFLOP/s)
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import threading
+import time
+
+import numpy as np
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, 2.5 PFLOP/s
+METRIC = "weight GB/s and % HBM roofline (M=1 INT4 GEMV); decode tok/s equiv for 7B/32B stacks"
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=50)
+    p.add_argument("--warmup", type=int, default=5)
+    p.add_argument("--config", default="qwen7b-decode",
+                   choices=["gemv-512", "qwen7b-decode", "qwen7b-batch", "qwen32b-decode", "qwen7b-prefill"])
+    p.add_argument("--m", type=int, default=None, help="activation rows (qwen7b-batch)")
+    p.add_argument("--launch", default="graph", choices=["graph", "eager"])
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--layers", type=int, default=None, help="override the layer count (profiling)")
+    return p.parse_args()
+
+
+class Stack:
+    """Device-resident weights, activations and outputs of one workload."""
+
+    def __init__(self, cfg: str, m: int | None, layers: int | None, torch, zq, synth):
+        self.cfg, self.torch, self.zq = cfg, torch, zq
+        dev = torch.device("cuda:0")
+        if cfg == "gemv-512":
+            shapes, L, bits_of, group, xdt, self.m = [("w", 512, 512)], 1, (lambda l: 4), 0, "f16", 1
+        elif cfg == "qwen7b-decode":
+            shapes, L, bits_of, group, xdt, self.m = synth.QWEN25_7B, 28, (lambda l: 4), 128, "f16", 1
+        elif cfg == "qwen7b-batch":
+            shapes, L, bits_of, group, xdt, self.m = synth.QWEN25_7B, 28, (lambda l: 4), 128, "bf16", m or 8
+        elif cfg == "qwen32b-decode":
+            shapes, L, bits_of, group, xdt, self.m = synth.QWEN25_32B, 64, (lambda l: 4), 128, "f16", 1
+        else:
+            shapes, L, bits_of, group, xdt, self.m = (synth.QWEN25_7B, 28, (lambda l: synth.layer_bits(5, l)),
+                                                      0, "bf16", 2048)
+        if layers:
+            L = layers
+        self.layers, self.shapes, self.group, self.xdt = L, shapes, group, xdt
+        self.launches = []   # (zq_weight, x tensor, y tensor)
+        self.weight_bytes = 0
+        self.flops = 0
+        seed = 0
+        for l in range(L):
+            bits = bits_of(l)
+            for name, n, k in shapes:
+                seed += 1
+                packed = synth.device_uniform_bytes(n * k * bits // 8, 1000003 * seed, dev)
+                ns = 1 if group == 0 else n * k // 128
+                if cfg == "gemv-512":
+                    scales = torch.tensor([0.02], dtype=torch.float16, device=dev)
+                else:
+                    scales = synth.device_scales_abs_normal(ns, 2000003 * seed, dev)
+                x = synth.device_normal((self.m, k), xdt, 3000003 * seed, dev)
+                y = torch.empty((self.m, n), dtype=torch.float32, device=dev)
+                W = zq.ZqWeight(bits, group, n, k, packed, scales)
+                self.launches.append((W, x, y))
+                self.weight_bytes += W.nbytes
+                self.flops += 2 * self.m * n * k
+        torch.cuda.synchronize()
+        L_ = zq.lib()
+        self._fn = L_.zq_gemm
+        self._descs = [W.desc() for W, _, _ in self.launches]
+        xt = zq.F16 if xdt == "f16" else zq.BF16
+        self._args = [(ctypes.byref(d), x.data_ptr(), xt, self.m, x.stride(0), y.data_ptr(), zq.F32,
+                       y.stride(0)) for d, (_, x, y) in zip(self._descs, self.launches)]
+
+    def step(self):
+        s = self.torch.cuda.current_stream().cuda_stream
+        fn = self._fn
+        for a in self._args:
+            st = fn(*a, s)
+            if st:
+                raise RuntimeError(f"zq_gemm failed: {self.zq.lib().zq_last_error().decode()}")
+
+    def step_timed_launches(self, ev):
+        """eager step with an event pair around every launch"""
+        s = self.torch.cuda.current_stream().cuda_stream
+        fn = self._fn
+        for a in self._args:
+            e0, e1 = ev()
+            e0.record()
+            fn(*a, s)
+            e1.record()
+            yield e0, e1
+
+
+def cpu_baseline(stack: Stack, torch, synth, budget_s: float = 12.0):
+    """The fp64 oracle on the host cores over a bounded sample of the same stack."""
+    from oracle import oracle as O
+    threads = min(len(os.sched_getaffinity(0)), 16)
+    done_bytes = 0
+    cpu_seconds = 0.0
+    wall = 0.0
+    used_layers = 0
+    per_layer = len(stack.shapes)
+    xdt = stack.xdt
+    xrows = min(stack.m, 16)  # prefill: 16 token rows (the work is linear in m)
+    for l in range(stack.layers):
+        jobs = []
+        for W, x, _ in stack.launches[l * per_layer:(l + 1) * per_layer]:
+            p = W.packed.cpu().numpy().reshape(W.n, -1)
+            sc = W.scales.view(torch.int16).cpu().numpy().view(np.uint16)
+            xh = x[:xrows].view(torch.int16).cpu().numpy().view(np.uint16)
+            bounds = np.linspace(0, W.n, threads + 1).astype(np.int64)
+            for t in range(threads):
+                r0, r1 = int(bounds[t]), int(bounds[t + 1])
+                if r1 > r0:
+                    s_rows = sc if W.group == 0 else sc.reshape(W.n, -1)[r0:r1]
+                    jobs.append((p[r0:r1], W.bits, s_rows, W.group, r1 - r0, W.k, xh, xdt))
+        # one thread per core; each runs its share of rows of every projection
+        per_thread = [jobs[i::threads] for i in range(threads)]
+
+        def work(js):
+            for (pp, bits, ss, grp, n, k, xh_, xd) in js:
+                O.gemm(pp, bits, ss, grp, n, k, xh_, xd)
+
+        ths = [threading.Thread(target=work, args=(js,)) for js in per_thread]
+        t0 = time.perf_counter()
+        c0 = time.process_time()
+        for t in ths:
+            t.start()
+        for t in ths:
+            t.join()
+        wall += time.perf_counter() - t0
+        cpu_seconds += time.process_time() - c0
+        used_layers += 1
+        done_bytes += sum(W.nbytes for W, _, _ in stack.launches[l * per_layer:(l + 1) * per_layer])
+        if cpu_seconds >= budget_s:
+            break
+    if stack.cfg == "qwen7b-prefill":
+        flops = sum(2 * xrows * W.n * W.k for W, _, _ in stack.launches[:used_layers * per_layer])
+        value, unit = flops / wall / 1e12, "TFLOP/s"
+    else:
+        value, unit = done_bytes / wall / 1e9, "GB/s"
+    return {"value": round(value, 4), "unit": unit, "cores": threads, "kind": "oracle",
+            "sample": f"first {used_layers} of {stack.layers} layers (all {per_layer} projections, "
+                      f"m={xrows} of {stack.m}), {cpu_seconds:.1f} CPU-s over {wall:.2f} s wall"}
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(f"bench.py: this build runs on one GPU only; --gpus {a.gpus} is not supported "
+              "(the sharded path is described in DESIGN.md)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from weight_quantized_amd import synth, zq
+    zq.lib()
+    if a.config == "qwen7b-prefill" and a.steps == 50:
+        a.steps = 10
+    stack = Stack(a.config, a.m, a.layers, torch, zq, synth)
+
+    # ---- timed region
+    graph = None
+    if a.launch == "graph":
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            stack.step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            stack.step()
+        run = graph.replay
+    else:
+        run = stack.step
+    for _ in range(a.warmup):
+        run()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record()
+    for _ in range(a.steps):
+        run()
+    e1.record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - w0) * 1e3 / a.steps
+    ms = e0.elapsed_time(e1) / a.steps
+
+    # ---- per-launch kernel durations (event pairs on the launch stream), same number of steps
+    torch.cuda.synchronize()
+    pairs = []
+    mk = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    for _ in range(max(1, min(a.steps, 20))):
+        pairs.extend(stack.step_timed_launches(mk))
+    torch.cuda.synchronize()
+    durs_ms = np.array([p0.elapsed_time(p1) for p0, p1 in pairs])
+    launches = len(stack.launches)
+    avg_launch_ms = float(durs_ms.mean())
+
+    out = {"metric": METRIC, "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
+           "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": None, "dtype": "f16" if stack.xdt == "f16" else "bf16", "data": "synthetic"}
+    per_layer_us = ms * 1e3 / stack.layers
+    if a.config == "qwen7b-prefill":
+        tfs = stack.flops / (ms * 1e-3) / 1e12
+        kern_tfs = (stack.flops / launches) / (avg_launch_ms * 1e-3) / 1e12
+        out.update({"metric": "prefill TFLOP/s and % bf16 MFMA roofline (mixed INT2/4/8 stack, M=2048)",
+                    "value": round(tfs, 2), "unit": "TFLOP/s",
+                    "mfma_frac": round(tfs / MFMA_BF16_PEAK_TFS, 4),
+                    "us_per_layer": round(per_layer_us, 2),
+                    "roofline": {"bound": "mfma", "achieved": round(kern_tfs, 2), "peak": MFMA_BF16_PEAK_TFS,
+                                 "unit": "TFLOP/s", "frac": round(kern_tfs / MFMA_BF16_PEAK_TFS, 4),
+                                 "traffic": None}})
+    else:
+        gbs = stack.weight_bytes / (ms * 1e-3) / 1e9
+        kern_gbs = (stack.weight_bytes / launches) / (avg_launch_ms * 1e-3) / 1e9
+        out.update({"value": round(gbs, 1), "unit": "GB/s", "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+                    "us_per_layer": round(per_layer_us, 3),
+                    "tok_s_equiv": round(stack.m / (ms * 1e-3), 1),
+                    "roofline": {"bound": "hbm", "achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS,
+                                 "unit": "GB/s", "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
+                                 "traffic": None}})
+    out["config"] = {"workload": {
+        "gemv-512": "single 512x512 INT4 GEMV, per-tensor fp16 scale 0.02, M=1, fp16 x",
+        "qwen7b-decode": "Qwen2.5-7B-shaped decode stack: 28 layers x 7 projections, M=1, INT4 group-128, fp16 x",
+        "qwen7b-batch": f"Qwen2.5-7B-shaped stack, M={stack.m}, INT4 group-128, bf16 x",
+        "qwen32b-decode": "Qwen2.5-32B-shaped decode stack: 64 layers x 7 projections, M=1, INT4 group-128, fp16 x",
+        "qwen7b-prefill": "Qwen2.5-7B-shaped prefill stack, per-layer INT2/INT4/INT8, per-tensor scale, M=2048, bf16 x",
+    }[a.config], "layers": stack.layers, "m": stack.m, "launches_per_step": launches,
+        "weight_bytes_per_step": stack.weight_bytes, "launch": a.launch,
+        "wall_ms_per_step": round(wall_ms, 5), "avg_kernel_us": round(avg_launch_ms * 1e3, 3)}
+    if not a.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(stack, torch, synth)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
