@@ -41,7 +41,12 @@ def parse():
     p.add_argument("--config", default="qwen7b-decode",
                    choices=["gemv-512", "qwen7b-decode", "qwen7b-batch", "qwen32b-decode", "qwen7b-prefill"])
     p.add_argument("--m", type=int, default=None, help="activation rows (qwen7b-batch)")
-    p.add_argument("--launch", default="graph", choices=["graph", "eager"])
+    p.add_argument("--launch", default=None, choices=["plan", "graph", "eager"],
+                   help="plan: one resident launch per step (m <= 4, the default there); "
+                        "graph: the per-projection launches replayed as a HIP graph")
+    p.add_argument("--order", default="chained", choices=["chained", "independent"],
+                   help="plan phases: chained = q,k,v -> o -> gate,up -> down per layer (each phase "
+                        "waits for the previous one); independent = every product of the step at once")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--layers", type=int, default=None, help="override the layer count (profiling)")
     return p.parse_args()
@@ -94,6 +99,28 @@ class Stack:
         xt = zq.F16 if xdt == "f16" else zq.BF16
         self._args = [(ctypes.byref(d), x.data_ptr(), xt, self.m, x.stride(0), y.data_ptr(), zq.F32,
                        y.stride(0)) for d, (_, x, y) in zip(self._descs, self.launches)]
+        self.plan = None
+
+    def make_plan(self, order: str):
+        """one resident launch per step. chained: the decoder-layer phases
+        q,k,v -> o -> gate,up -> down, each waiting for the previous phase;
+        independent: every product of the step in one phase, in an order that
+        groups equal K (all q,k,v,o,gate,up of the step, then all down)."""
+        phase_of = {"q": 0, "k": 0, "v": 0, "o": 1, "gate": 2, "up": 2, "down": 3, "w": 0}
+        per_layer = len(self.shapes)
+        items = []
+        for i, (W, x, y) in enumerate(self.launches):
+            l, name = divmod(i, per_layer)
+            items.append((l, name, (W, x, y)))
+        if order == "chained":
+            probs = [(W, x, y, 4 * l + phase_of[self.shapes[nm][0]]) for l, nm, (W, x, y) in items]
+        else:
+            items.sort(key=lambda t: (t[2][0].k, t[0], t[1]))
+            probs = [(W, x, y, 0) for l, nm, (W, x, y) in items]
+        self.plan = self.zq.Plan(probs)
+
+    def plan_step(self):
+        self.plan.run()
 
     def step(self):
         s = self.torch.cuda.current_stream().cuda_stream
@@ -181,9 +208,14 @@ def main():
         a.steps = 10
     stack = Stack(a.config, a.m, a.layers, torch, zq, synth)
 
+    if a.launch is None:
+        a.launch = "plan" if stack.m <= 4 else "graph"
     # ---- timed region
     graph = None
-    if a.launch == "graph":
+    if a.launch == "plan":
+        stack.make_plan(a.order)
+        run = stack.plan_step
+    elif a.launch == "graph":
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
@@ -213,11 +245,23 @@ def main():
     torch.cuda.synchronize()
     pairs = []
     mk = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-    for _ in range(max(1, min(a.steps, 20))):
-        pairs.extend(stack.step_timed_launches(mk))
+    if a.launch == "plan":
+        # the dominant kernel is the plan's single resident launch
+        for _ in range(a.steps):
+            p0, p1 = mk()
+            p0.record()
+            stack.plan_step()
+            p1.record()
+            pairs.append((p0, p1))
+        launches = 1
+    else:
+        for _ in range(max(1, min(a.steps, 20))):
+            pairs.extend(stack.step_timed_launches(mk))
+        launches = len(stack.launches)
     torch.cuda.synchronize()
     durs_ms = np.array([p0.elapsed_time(p1) for p0, p1 in pairs])
-    launches = len(stack.launches)
+    if stack.plan is not None:
+        stack.plan.check()
     avg_launch_ms = float(durs_ms.mean())
 
     out = {"metric": METRIC, "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
@@ -249,8 +293,9 @@ def main():
         "qwen7b-batch": f"Qwen2.5-7B-shaped stack, M={stack.m}, INT4 group-128, bf16 x",
         "qwen32b-decode": "Qwen2.5-32B-shaped decode stack: 64 layers x 7 projections, M=1, INT4 group-128, fp16 x",
         "qwen7b-prefill": "Qwen2.5-7B-shaped prefill stack, per-layer INT2/INT4/INT8, per-tensor scale, M=2048, bf16 x",
-    }[a.config], "layers": stack.layers, "m": stack.m, "launches_per_step": launches,
-        "weight_bytes_per_step": stack.weight_bytes, "launch": a.launch,
+    }[a.config], "layers": stack.layers, "m": stack.m,
+        "weight_bytes_per_step": stack.weight_bytes, "launch": a.launch, "order": a.order if a.launch == "plan" else "stream",
+        "launches_per_step": 2 if a.launch == "plan" else len(stack.launches),
         "wall_ms_per_step": round(wall_ms, 5), "avg_kernel_us": round(avg_launch_ms * 1e3, 3)}
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(stack, torch, synth)

@@ -168,6 +168,55 @@ zq_status zq_gemv(const zq_weight* W, const void* x, zq_dtype x_dtype, void* y,
 zq_status zq_gemm(const zq_weight* W, const void* X, zq_dtype x_dtype, int64_t m,
                   int64_t ldx, void* Y, zq_dtype y_dtype, int64_t ldy, void* stream);
 
+/*
+ * Plans: many decode-step products in one launch.
+ * [wiki, section "Оркестратор и GPU-ядра": the decode launch sequence is
+ * captured as one CUDA/HIP graph to cut launch cost.] On gfx950 a dependent
+ * kernel launch costs more than streaming a small weight matrix, so a plan
+ * runs a whole list of products in one resident launch instead.
+ *
+ * zq_problem   one product Y = X * dequant(W)^T, fields as in zq_gemm
+ *              (m is the plan's). Problems run in array order of `phase`
+ *              (non-decreasing in the array): every problem of phase p starts
+ *              its arithmetic only after all problems of phases < p have
+ *              stored their outputs, so Y of one phase may be X of the next
+ *              (q,k,v -> o -> gate,up -> down of a decoder layer). Problems of
+ *              one phase are independent and must not write what another one
+ *              of that phase reads. Consecutive problems of a phase that share
+ *              k, bits, group and x dtype (up to 4) are streamed as one row
+ *              space; problems that share an activation buffer stage it once.
+ * zq_plan_create  validates every problem (as zq_gemm does), requires
+ *              1 <= m <= 4, packed rows whose byte length is a multiple of 256
+ *              and 16-byte aligned pointers (ZQ_ERR_UNSUPPORTED otherwise),
+ *              copies the list to device memory and allocates two device words
+ *              for the phase counter. Pointers inside the problems are used at
+ *              every run: the caller keeps those buffers alive.
+ * zq_plan_run  enqueues the plan on `stream` (two launches: a counter reset
+ *              and one cooperative kernel with one workgroup per CU);
+ *              allocates nothing. Runs of one plan on different streams at
+ *              the same time race on its counter.
+ * zq_plan_check synchronises the device and reports ZQ_ERR_HIP if a phase
+ *              wait in an earlier run gave up (its outputs are then invalid).
+ * zq_plan_destroy frees the plan's device memory (synchronises the device).
+ */
+typedef struct zq_problem {
+  zq_weight w;
+  const void* x;
+  zq_dtype x_dtype;
+  int64_t ldx;
+  void* y;
+  zq_dtype y_dtype;
+  int64_t ldy;
+  int32_t phase;
+} zq_problem;
+
+typedef struct zq_plan_s* zq_plan;
+
+zq_status zq_plan_create(const zq_problem* problems, int count, int64_t m, zq_plan* plan_out);
+zq_status zq_plan_run(zq_plan plan, void* stream);
+zq_status zq_plan_check(zq_plan plan);
+zq_status zq_plan_destroy(zq_plan plan);
+
 /* Static description of a status code. */
 const char* zq_status_string(zq_status s);
 

@@ -1,0 +1,140 @@
+"""Plans (many products in one resident launch) against the oracle and against
+single zq_gemm calls; phase order checked with a real output -> input chain."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import oracle as O
+from weight_quantized_amd import synth
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+zq = None
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    global zq
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from weight_quantized_amd import zq as _zq
+    _zq.lib()
+    zq = _zq
+
+
+def weight(bits, group, n, k, seed, codes=None, scales=None):
+    g = synth.rng(seed)
+    q = synth.codes_uniform(g, n, k, bits) if codes is None else codes
+    s = synth.scales_abs_normal(g, O.num_scales(group, n, k)) if scales is None else scales
+    p = O.pack(q, bits)
+    W = zq.ZqWeight(bits, group, n, k, torch.from_numpy(p.reshape(-1)).to(DEV),
+                    torch.from_numpy(s.view(np.float16)).to(DEV))
+    return q, s, p, W
+
+
+def x_dev(x, xdt):
+    if xdt == "bf16":
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(DEV)
+    return torch.from_numpy(x).to(DEV)
+
+
+def x64(x, xdt):
+    if xdt == "bf16":
+        return torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    return x.astype(np.float64)
+
+
+@pytest.mark.parametrize("m", [1, 2, 4])
+def test_plan_matches_oracle_and_single_calls(m):
+    # mixed formats inside one phase are split into segments without a barrier
+    # a miniature decoder layer stack with mixed formats: (bits, group, n, k, xdt, phase)
+    spec = [(4, 128, 512, 1024, "f16", 0), (4, 128, 256, 1024, "f16", 0), (8, 0, 300, 2048, "f16", 1),
+            (2, 128, 640, 1024, "bf16", 2), (4, 0, 1000, 512, "bf16", 2), (8, 128, 96, 4096, "bf16", 3),
+            (4, 128, 3584, 3584, "f16", 4)]
+    probs, refs = [], []
+    for i, (bits, group, n, k, xdt, ph) in enumerate(spec):
+        q, s, p, W = weight(bits, group, n, k, seed=100 + i)
+        x = synth.normal(synth.rng(200 + i), (m, k), xdt)
+        Y = torch.full((m, n), float("nan"), device=DEV)
+        probs.append((W, x_dev(x, xdt), Y, ph))
+        refs.append((q, s, p, x, xdt, group, bits, n, k))
+    plan = zq.Plan(probs)
+    for rep in range(3):
+        for _, _, Y, _ in probs:
+            Y.fill_(float("nan"))
+        plan.run()
+        torch.cuda.synchronize()
+        plan.check()
+        if rep == 0:
+            first = [Y.clone() for _, _, Y, _ in probs]
+        for (W, X, Y, _), (q, s, p, x, xdt, group, bits, n, k), f in zip(probs, refs, first):
+            assert torch.equal(Y, f)                         # identical across runs
+    for (W, X, Y, _), (q, s, p, x, xdt, group, bits, n, k) in zip(probs, refs):
+        single = zq.gemm(W, X)
+        torch.cuda.synchronize()
+        assert torch.equal(single, Y)                        # same kernel, same split
+        yref = O.gemm(p, bits, s, group, n, k, x, xdt)
+        xn = np.sqrt((x64(x, xdt) ** 2).sum(1))[:, None]
+        tol = 2e-3 * xn * np.abs(O.dequant(q, group, s)).max(1)[None, :] + 1e-3 * np.abs(yref)
+        assert np.all(np.abs(Y.double().cpu().numpy() - yref) <= tol)
+
+
+def test_plan_phase_order_with_output_feeding_input():
+    """phase 0: y1 = W1 x0 (fp16 out, exact integers); phase 1: y2 = W2 y1.
+    y1 is NaN before every run: phase 1 must read the values phase 0 stored."""
+    k1, n1, n2 = 1024, 2048, 700
+    g = synth.rng(5)
+    q1 = g.integers(-1, 2, size=(n1, k1), dtype=np.int8)
+    q2 = synth.codes_uniform(g, n2, n1, 4)
+    one = np.full(n1 * k1 // 128, 0x3C00, dtype=np.uint16)
+    _, s1, p1, W1 = weight(4, 128, n1, k1, 0, codes=q1, scales=one)
+    _, s2, p2, W2 = weight(4, 128, n2, n1, 0, codes=q2, scales=np.full(n2 * n1 // 128, 0x3C00, dtype=np.uint16))
+    x0 = g.integers(-1, 2, size=(1, k1)).astype(np.float16)
+    X0 = torch.from_numpy(x0).to(DEV)
+    Y1 = torch.empty((1, n1), dtype=torch.float16, device=DEV)
+    Y2 = torch.empty((1, n2), dtype=torch.float32, device=DEV)
+    plan = zq.Plan([(W1, X0, Y1, 0), (W2, Y1, Y2, 1)])
+    y1_ref = O.gemm(p1, 4, s1, 128, n1, k1, x0, "f16")           # |y1| <= 1024: exact in fp16
+    y2_ref = O.gemm(p2, 4, s2, 128, n2, n1, y1_ref.astype(np.float16), "f16")
+    for _ in range(5):
+        Y1.fill_(float("nan"))
+        Y2.fill_(0)
+        plan.run()
+        torch.cuda.synchronize()
+        assert np.array_equal(Y1.double().cpu().numpy(), y1_ref)
+        assert np.array_equal(Y2.double().cpu().numpy(), y2_ref)
+    plan.check()
+
+
+def test_plan_many_phases_on_one_stream_with_other_work():
+    probs = []
+    for i in range(24):
+        _, _, _, W = weight(4, 128, 512, 512, seed=i)
+        X = torch.randn(1, 512, device=DEV).half()
+        probs.append((W, X, torch.empty((1, 512), device=DEV), i))
+    plan = zq.Plan(probs)
+    outs = []
+    for _ in range(4):
+        plan.run()
+        torch.cuda.synchronize()
+        outs.append(torch.cat([Y for _, _, Y, _ in probs]).clone())
+        probs[0][2].fill_(1.0)   # unrelated work between runs
+    assert all(torch.equal(outs[0], o) for o in outs[1:])
+    plan.check()
+
+
+def test_plan_validation():
+    _, _, _, Wbad = weight(4, 128, 64, 384, seed=1)      # 192-byte rows: not a multiple of 256
+    X = torch.zeros((1, 384), dtype=torch.float16, device=DEV)
+    with pytest.raises(zq.ZqError) as e:
+        zq.Plan([(Wbad, X, torch.empty((1, 64), device=DEV), 0)])
+    assert e.value.status == zq.ERR_UNSUPPORTED
+    _, _, _, W = weight(4, 128, 64, 512, seed=2)
+    X = torch.zeros((1, 512), dtype=torch.float16, device=DEV)
+    with pytest.raises(zq.ZqError) as e:
+        zq.Plan([(W, X, torch.empty((1, 64), device=DEV), 1), (W, X, torch.empty((1, 64), device=DEV), 0)])
+    assert e.value.status == zq.ERR_INVALID_ARG
+    X5 = torch.zeros((5, 512), dtype=torch.float16, device=DEV)
+    with pytest.raises(zq.ZqError) as e:
+        zq.Plan([(W, X5, torch.empty((5, 64), device=DEV), 0)])
+    assert e.value.status == zq.ERR_UNSUPPORTED

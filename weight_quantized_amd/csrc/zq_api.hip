@@ -5,10 +5,11 @@
 #include <stdio.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <vector>
 
-#include "../../include/zq.h"
+#include "zq.h"
 #include "zq_device.hpp"
 #include "zq_internal.hpp"
 
@@ -206,13 +207,231 @@ zq_status zq_gemm(const zq_weight* W, const void* X, zq_dtype x_dtype, int64_t m
   const int64_t rowbytes = W->k * W->bits / 8;
   const bool aligned16 = ((uintptr_t)W->packed & 15) == 0 && rowbytes % 16 == 0 &&
                          ((uintptr_t)X & 15) == 0 && (m == 1 || (ldx * 2) % 16 == 0);
-  if (m <= 4 && aligned16 && zq::gemv_valu_lds_bytes(W->bits, m, W->k) <= 64 * 1024)
+  if (m <= 4 && aligned16 && zq::stream_supported(W->bits, W->group, m, W->n, W->k)) {
+    zq::StreamProblem p{};
+    p.packed = a.packed;
+    p.scales = a.scales;
+    p.x = a.x;
+    p.y = a.y;
+    p.n = a.n;
+    p.k = a.k;
+    p.ldx = a.ldx;
+    p.ldy = a.ldy;
+    p.bits = a.bits;
+    p.group = a.group;
+    p.xt = a.xt;
+    p.yt = a.yt;
+    p.row_off = 0;
+    e = zq::launch_stream_single(p, m, s);
+  } else if (m <= 4 && aligned16 && zq::gemv_valu_lds_bytes(W->bits, m, W->k) <= 64 * 1024)
     e = zq::launch_gemv_valu(a);
   else if (aligned16 && zq::gemm_mfma_supported(a))
     e = zq::launch_gemm_mfma(a);
   else
     e = zq::launch_gemm_general(a);
   return e == hipSuccess ? ok() : hip_fail(e, "gemm launch");
+}
+
+}  // extern "C"
+
+struct zq_plan_s {
+  zq::StreamPhase* segs = nullptr;     // device
+  zq::StreamProblem* probs = nullptr;  // device
+  int2* ranges = nullptr;              // device: [segment][workgroup] {first, last}
+  uint32_t* sync = nullptr;            // device: counter, error word
+  int nseg = 0;
+  int64_t m = 1;
+  int variant = 12;  // one format for all segments, or 12 for a mix
+  size_t lds = 0;
+};
+
+namespace {
+// products of segment `sg` touched by workgroup w of G: rows [w*N/G, (w+1)*N/G)
+void seg_ranges(const zq::StreamPhase& sg, const std::vector<zq::StreamProblem>& probs, int G,
+                std::vector<int2>& out) {
+  const int64_t N = sg.n_total;
+  int lo = 0;
+  for (int w = 0; w < G; ++w) {
+    const int64_t r0 = w * N / G, r1 = (w + 1) * N / G;
+    if (r1 == r0) {
+      out.push_back(make_int2(0, 0));
+      continue;
+    }
+    while (lo + 1 < sg.count && probs[sg.first + lo + 1].row_off <= r0) ++lo;
+    int hi = lo;
+    while (hi + 1 < sg.count && probs[sg.first + hi + 1].row_off < r1) ++hi;
+    out.push_back(make_int2(lo, hi));
+  }
+}
+}  // namespace
+
+extern "C" {
+
+zq_status zq_plan_create(const zq_problem* problems, int count, int64_t m, zq_plan* plan_out) {
+  if (!plan_out) return fail(ZQ_ERR_INVALID_ARG, "null plan_out");
+  *plan_out = nullptr;
+  if (count < 1 || !problems) return fail(ZQ_ERR_INVALID_ARG, "empty problem list");
+  if (m < 1 || m > 4) return fail(ZQ_ERR_UNSUPPORTED, "plans take 1 <= m <= 4 (m=%lld)", (long long)m);
+  std::vector<zq::StreamProblem> probs(count);
+  std::vector<zq::StreamPhase> segs;
+  for (int i = 0; i < count; ++i) {
+    const zq_problem& q = problems[i];
+    zq_status st = check_weight(&q.w);
+    if (st) return fail(st, "problem %d: %s", i, g_err);
+    if (i > 0 && q.phase < problems[i - 1].phase)
+      return fail(ZQ_ERR_INVALID_ARG, "problem %d: phases must not decrease", i);
+    if (q.x_dtype != ZQ_F16 && q.x_dtype != ZQ_BF16)
+      return fail(ZQ_ERR_INVALID_ARG, "problem %d: x_dtype must be F16 or BF16", i);
+    if (q.y_dtype != ZQ_F32 && q.y_dtype != ZQ_F16 && q.y_dtype != ZQ_BF16)
+      return fail(ZQ_ERR_INVALID_ARG, "problem %d: y_dtype must be F32, F16 or BF16", i);
+    if (q.ldx < q.w.k || q.ldy < q.w.n) return fail(ZQ_ERR_INVALID_ARG, "problem %d: ldx < k or ldy < n", i);
+    if (q.w.n == 0 || q.w.k == 0 || !q.x || !q.y)
+      return fail(ZQ_ERR_UNSUPPORTED, "problem %d: empty shapes and null pointers are not planned", i);
+    const bool aligned = ((uintptr_t)q.w.packed & 15) == 0 && ((uintptr_t)q.x & 15) == 0 &&
+                         (m == 1 || (q.ldx * 2) % 16 == 0);
+    if (!aligned || !zq::stream_supported(q.w.bits, q.w.group, m, q.w.n, q.w.k))
+      return fail(ZQ_ERR_UNSUPPORTED, "problem %d: needs 16-byte alignment, rows of 256-byte multiples "
+                  "and activations that fit in LDS", i);
+    const int xt = q.x_dtype == ZQ_F16 ? zq::XF16 : zq::XBF16;
+    // a new segment when the phase or the format changes
+    const bool same_phase = i > 0 && q.phase == problems[i - 1].phase;
+    bool new_segment = !same_phase;
+    if (same_phase) {
+      const zq::StreamPhase& sg = segs.back();
+      new_segment = sg.k != q.w.k || sg.bits != q.w.bits || sg.group != q.w.group || sg.xt != xt;
+    }
+    if (new_segment) {
+      zq::StreamPhase sg{};
+      sg.first = i;
+      sg.k = q.w.k;
+      sg.bits = q.w.bits;
+      sg.group = q.w.group;
+      sg.xt = xt;
+      sg.wait = (i > 0 && !same_phase) ? 1 : 0;
+      segs.push_back(sg);
+    }
+    zq::StreamPhase& sg = segs.back();
+    zq::StreamProblem& p = probs[i];
+    p = zq::StreamProblem{};
+    p.packed = (const uint8_t*)q.w.packed;
+    p.scales = q.w.scales;
+    p.x = (const uint16_t*)q.x;
+    p.y = q.y;
+    p.n = q.w.n;
+    p.k = q.w.k;
+    p.ldx = q.ldx;
+    p.ldy = q.ldy;
+    p.row_off = sg.n_total;
+    p.bits = q.w.bits;
+    p.group = q.w.group;
+    p.xt = xt;
+    p.yt = q.y_dtype == ZQ_F32 ? zq::YF32 : q.y_dtype == ZQ_F16 ? zq::YF16 : zq::YBF16;
+    sg.count += 1;
+    sg.n_total += q.w.n;
+  }
+  // Split segments whose workgroup ranges would stage too many activation
+  // buffers for LDS: halve them (no wait between the halves) until they fit.
+  const int G = zq::stream_grid();
+  std::vector<zq::StreamPhase> fitted;
+  std::vector<int2> ranges;
+  size_t lds = 0;
+  for (size_t si = 0; si < segs.size(); ++si) {
+    std::vector<zq::StreamPhase> todo{segs[si]};
+    while (!todo.empty()) {
+      zq::StreamPhase sg = todo.back();
+      todo.pop_back();
+      // row offsets relative to this (possibly split) segment
+      int64_t off = 0;
+      for (int i = 0; i < sg.count; ++i) {
+        probs[sg.first + i].row_off = off;
+        off += probs[sg.first + i].n;
+      }
+      sg.n_total = off;
+      std::vector<int2> r;
+      seg_ranges(sg, probs, G, r);
+      int maxrec = 1;
+      for (const int2& v : r) maxrec = std::max(maxrec, v.y - v.x + 1);
+      const size_t need = zq::stream_lds_bytes(sg.bits, m, sg.k, maxrec);
+      if (need > zq::STREAM_LDS_MAX) {
+        if (sg.count == 1)
+          return fail(ZQ_ERR_UNSUPPORTED, "problem %d needs %zu bytes of LDS (max %zu)", sg.first, need,
+                      zq::STREAM_LDS_MAX);
+        zq::StreamPhase a = sg, b = sg;
+        a.count = sg.count / 2;
+        b.first = sg.first + a.count;
+        b.count = sg.count - a.count;
+        b.wait = 0;
+        todo.push_back(b);  // processed after a (stack order)
+        todo.push_back(a);
+        continue;
+      }
+      fitted.push_back(sg);
+      ranges.insert(ranges.end(), r.begin(), r.end());
+      lds = std::max(lds, need);
+    }
+  }
+  int variant = -1;
+  for (const zq::StreamPhase& sg : fitted) {
+    const int v = zq::stream_variant_of(sg.xt, sg.bits, sg.group);
+    variant = (variant == -1 || variant == v) ? v : 12;
+  }
+  zq_plan_s* plan = new zq_plan_s;
+  plan->nseg = (int)fitted.size();
+  plan->m = m;
+  plan->lds = lds;
+  plan->variant = variant;
+  hipError_t e = hipMalloc(&plan->segs, sizeof(zq::StreamPhase) * fitted.size());
+  if (e == hipSuccess) e = hipMalloc(&plan->probs, sizeof(zq::StreamProblem) * probs.size());
+  if (e == hipSuccess) e = hipMalloc(&plan->ranges, sizeof(int2) * ranges.size());
+  if (e == hipSuccess) e = hipMalloc(&plan->sync, 2 * sizeof(uint32_t));
+  if (e == hipSuccess)
+    e = hipMemcpy(plan->segs, fitted.data(), sizeof(zq::StreamPhase) * fitted.size(), hipMemcpyHostToDevice);
+  if (e == hipSuccess)
+    e = hipMemcpy(plan->probs, probs.data(), sizeof(zq::StreamProblem) * probs.size(), hipMemcpyHostToDevice);
+  if (e == hipSuccess)
+    e = hipMemcpy(plan->ranges, ranges.data(), sizeof(int2) * ranges.size(), hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemset(plan->sync, 0, 2 * sizeof(uint32_t));
+  if (e != hipSuccess) {
+    (void)hipFree(plan->segs);
+    (void)hipFree(plan->probs);
+    (void)hipFree(plan->ranges);
+    (void)hipFree(plan->sync);
+    delete plan;
+    return hip_fail(e, "plan allocation");
+  }
+  *plan_out = plan;
+  return ok();
+}
+
+zq_status zq_plan_run(zq_plan plan, void* stream) {
+  if (!plan) return fail(ZQ_ERR_INVALID_ARG, "null plan");
+  hipError_t e = zq::launch_stream_plan(plan->segs, plan->nseg, plan->probs, plan->ranges, plan->m,
+                                        plan->variant, plan->lds, plan->sync, (hipStream_t)stream);
+  return e == hipSuccess ? ok() : hip_fail(e, "plan launch");
+}
+
+zq_status zq_plan_check(zq_plan plan) {
+  if (!plan) return fail(ZQ_ERR_INVALID_ARG, "null plan");
+  uint32_t w[2] = {0, 0};
+  hipError_t e = hipDeviceSynchronize();
+  if (e == hipSuccess) e = hipMemcpy(w, plan->sync, sizeof w, hipMemcpyDeviceToHost);
+  if (e != hipSuccess) return hip_fail(e, "plan check");
+  if (w[1]) return fail(ZQ_ERR_HIP, "a phase wait gave up: outputs of that run are invalid");
+  return ok();
+}
+
+zq_status zq_plan_destroy(zq_plan plan) {
+  if (!plan) return ok();
+  hipError_t e = hipDeviceSynchronize();
+  hipError_t e1 = hipFree(plan->segs);
+  if (e1 == hipSuccess) e1 = hipFree(plan->probs);
+  if (e1 == hipSuccess) e1 = hipFree(plan->ranges);
+  hipError_t e2 = hipFree(plan->sync);
+  delete plan;
+  if (e != hipSuccess) return hip_fail(e, "plan destroy sync");
+  if (e1 != hipSuccess) return hip_fail(e1, "plan destroy");
+  if (e2 != hipSuccess) return hip_fail(e2, "plan destroy");
+  return ok();
 }
 
 zq_status zq_gemv(const zq_weight* W, const void* x, zq_dtype x_dtype, void* y, zq_dtype y_dtype,

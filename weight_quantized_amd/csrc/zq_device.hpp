@@ -17,6 +17,17 @@ typedef float f16v __attribute__((ext_vector_type(16)));
 typedef uint32_t u4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u2 __attribute__((ext_vector_type(2)));
 
+// Global-address-space views of pointers that come out of structs: loads and
+// stores through generic pointers compile to FLAT instructions, which count
+// against both the vector-memory and the LDS counters and make the compiler
+// wait for every load in flight before any LDS access.
+template <class T>
+using gptr = __attribute__((address_space(1))) T*;
+template <class T>
+__device__ __forceinline__ gptr<T> to_global(T* p) {
+  return (gptr<T>)(p);
+}
+
 enum XType { XF16 = 1, XBF16 = 2 };
 enum YType { YF32 = 3, YF16 = 1, YBF16 = 2 };
 

@@ -31,6 +31,38 @@ struct GemmArgs {
   hipStream_t stream;
 };
 
+// One product of the persistent decode kernel (device pointers).
+struct StreamProblem {
+  const uint8_t* packed;
+  const uint16_t* scales;
+  const uint16_t* x;
+  void* y;
+  int64_t n, k, ldx, ldy;
+  int64_t row_off;  // first row in its segment's concatenated row space
+  int32_t bits, group, xt, yt;
+};
+// A segment of a plan: consecutive products of one phase that share k, bits,
+// group and activation type. wait = 1: the segment starts its arithmetic
+// only after every workgroup has stored all earlier segments' outputs.
+struct StreamPhase {
+  int32_t first, count;  // problems [first, first + count) of the problem table
+  int64_t n_total, k;
+  int32_t bits, group, xt, wait;
+};
+constexpr size_t STREAM_LDS_MAX = 160 * 1024;
+int stream_grid();  // workgroups of a stream launch (one per CU)
+// persistent, balanced kernel (1 <= m <= 4, rows of whole 256-byte steps)
+bool stream_supported(int bits, int group, int64_t m, int64_t n, int64_t k);
+size_t stream_lds_bytes(int bits, int64_t m, int64_t k, int nrec);
+int stream_variant_of(int xt, int bits, int group);
+hipError_t launch_stream_single(const StreamProblem& p, int64_t m, hipStream_t stream);
+// dev_ranges[s * stream_grid() + w] = {first, last} product (within segment s)
+// that workgroup w touches; variant: one format code (stream_variant_of) for
+// every segment, or 12 for a mix; sync = 2 device words (counter, error)
+hipError_t launch_stream_plan(const StreamPhase* dev_segs, int nseg, const StreamProblem* dev_probs,
+                              const int2* dev_ranges, int64_t m, int variant, size_t lds, uint32_t* sync,
+                              hipStream_t stream);
+
 // vector-ALU kernel for m <= 4 with x staged in LDS
 size_t gemv_valu_lds_bytes(int bits, int64_t m, int64_t k);
 hipError_t launch_gemv_valu(const GemmArgs& a);

@@ -1,0 +1,579 @@
+// zq_stream_impl.hpp -- persistent, load-balanced decode kernel (1..4
+// activation rows) for one weight matrix or for a whole list of them in one
+// launch. Host launchers: zq_stream.hip; instantiations: zq_stream_m1..m4.hip.
+//
+// Prior art: the wave-64 INT4 GEMV with 128-bit weight loads of the ZSE wiki
+// article ("ZSE - open-source движок для запуска LLM локально на GPU - 2026",
+// section "Оркестратор и GPU-ядра"), which also captures the decode launch
+// sequence in a graph to cut launch cost. On gfx950 every launch and every
+// dependent step costs microseconds, more than streaming a 7B k/v matrix, so
+// this kernel stays resident (one workgroup per CU) and streams a list of
+// products as a few long segments.
+//
+// A segment is a run of products that share K, code width, scale layout and
+// activation type; their rows are concatenated into one row space and
+// workgroup w streams rows [w*N/G, (w+1)*N/G) of it -- one contiguous range
+// that may cover several products. A segment may have to wait until every
+// workgroup has stored the outputs of the segments before it (a device-wide
+// counter), so outputs of one phase can feed the next; data that crosses such
+// a wait is stored and loaded with agent-coherent (sc1) accesses, and the
+// counter is a relaxed agent atomic after an s_waitcnt: an agent-scope
+// release/acquire fence writes back or invalidates the XCD's whole L2.
+//
+// Inside a workgroup's range:
+//   * the products it touches are described by records in LDS; the
+//     activations of each are staged in LDS in decoder order (see Decoder)
+//     with two sums per 16-byte chunk (even and odd k) that remove the
+//     decoder's constant offsets;
+//   * its 16-lane groups each get an equal, contiguous run of 16-chunk steps
+//     (a step = 256 contiguous bytes of one row), so work is balanced to one
+//     chunk per lane whatever the shapes;
+//   * every lane keeps ST_U chunks (and their group scales) in flight; loads
+//     are issued unconditionally -- past its run a lane re-reads a cached
+//     chunk and discards it -- so the compiler waits for exactly one load
+//     per step, and the main loop has a workgroup-uniform trip count;
+//   * a group reduces its 16 lane partials with four DPP steps whenever its
+//     run leaves a row: a row that lies inside the run is stored at once; a
+//     row split between runs leaves a tail partial and head partials that are
+//     summed in group order after the loop, so results are run-to-run
+//     identical.
+#pragma once
+#include "zq_device.hpp"
+#include "zq_internal.hpp"
+
+namespace zq {
+
+constexpr int ST_U = 8;
+// 1024 threads (16 waves, 128 VGPRs) for one activation row; 512 threads
+// (256 VGPRs) when each lane keeps 2..4 rows of partials.
+template <int MR>
+constexpr int st_threads() { return MR == 1 ? 1024 : 512; }
+
+// Fast decoder for the stream kernel.
+//  fp16 INT4: pairs (0,4),(2,6) put the nibble in the fraction's low bits
+//    (value 1024 + u), pairs (1,5),(3,7) in bits 7:4 (value 64 + u); one shift
+//    by 8 serves the upper two pairs. u = q + 8. Offsets: even k 1032, odd 72.
+//  fp16 INT8: bytes in the fraction's low 8 bits: value 1024 + u, u = q + 128.
+//  everything else: the generic Decoder (one offset for all k).
+template <int XT, int BITS>
+struct FastDec {
+  static constexpr float BE = (XT == XF16 && BITS == 4) ? 1032.f
+                              : (XT == XF16 && BITS == 8) ? 1152.f
+                                                          : Decoder<XT, BITS>::BIAS;
+  static constexpr float BO = (XT == XF16 && BITS == 4) ? 72.f : BE;
+  static __device__ __forceinline__ float dot(uint32_t v, const uint32_t* xq, float d) {
+    if constexpr (XT == XF16 && BITS == 4) {
+      const uint32_t t = v >> 8;
+      d = dot2<XF16>((v & 0x000F000Fu) | 0x64006400u, xq[0], d);
+      d = dot2<XF16>((v & 0x00F000F0u) | 0x54005400u, xq[1], d);
+      d = dot2<XF16>((t & 0x000F000Fu) | 0x64006400u, xq[2], d);
+      d = dot2<XF16>((t & 0x00F000F0u) | 0x54005400u, xq[3], d);
+      return d;
+    } else if constexpr (XT == XF16 && BITS == 8) {
+      d = dot2<XF16>((v & 0x00FF00FFu) | 0x64006400u, xq[0], d);
+      d = dot2<XF16>(((v >> 8) & 0x00FF00FFu) | 0x64006400u, xq[1], d);
+      return d;
+    } else {
+      using D = Decoder<XT, BITS>;
+      [&]<int... I>(std::integer_sequence<int, I...>) {
+        ((d = dot2<XT>(D::template pair<I>(v), xq[I], d)), ...);
+      }(std::make_integer_sequence<int, Codes<BITS>::PAIRS>{});
+      return d;
+    }
+  }
+};
+
+// One product as the workgroup sees it (LDS record, 64 bytes).
+struct ProdRec {
+  const uint8_t* wbase;   // packed - roff * rowbytes: index by segment row
+  const uint16_t* sbase;  // grouped: scales - roff * (k/128); per tensor: unused
+  const uint16_t* x;
+  void* y;
+  int64_t ldx, ldy;
+  int32_t roff, pend;     // rows [roff, pend) of the segment row space
+  int32_t yt;
+  float tscale;           // per-tensor scale (1 when grouped)
+};
+static_assert(sizeof(ProdRec) == 64, "LDS record layout");
+
+// LDS bytes of one workgroup's view of a segment touching nrec products
+__host__ __device__ inline size_t stream_seg_lds(int bits, int64_t mr, int64_t k, int nrec) {
+  const int64_t wpc = 128 / bits, pc = wpc / 8, C = k / wpc;
+  const int ng = mr == 1 ? 64 : 32;
+  return (size_t)nrec * 64 + (size_t)nrec * mr * C * (pc * 16 + 8) + (size_t)ng * (8 + 8 * mr);
+}
+
+// 16 bytes of activations, optionally with agent-coherent loads (the buffer
+// may have been written by another workgroup before the phase wait).
+__device__ __forceinline__ u4 load_x16(const uint16_t* p, bool coherent) {
+  if (!coherent) return *to_global(reinterpret_cast<const u4*>(p));
+  gptr<const uint32_t> q = to_global(reinterpret_cast<const uint32_t*>(p));
+  u4 r;
+  r[0] = __hip_atomic_load(q + 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  r[1] = __hip_atomic_load(q + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  r[2] = __hip_atomic_load(q + 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  r[3] = __hip_atomic_load(q + 3, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return r;
+}
+__device__ __forceinline__ uint16_t load_x2(const uint16_t* p, bool coherent) {
+  if (!coherent) return *to_global(p);
+  return __hip_atomic_load(to_global(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_y_coherent(void* y, int64_t idx, float v, int yt, bool coherent) {
+  if (yt == YF32) {
+    gptr<float> d = to_global(reinterpret_cast<float*>(y)) + idx;
+    if (coherent) __hip_atomic_store(d, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else *d = v;
+  } else {
+    const uint16_t h = yt == YF16 ? float_to_f16_bits(v) : float_to_bf16_bits(v);
+    gptr<uint16_t> d = to_global(reinterpret_cast<uint16_t*>(y)) + idx;
+    if (coherent) __hip_atomic_store(d, h, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else *d = h;
+  }
+}
+
+// Record of product p for a segment (device table entry or the single product).
+__device__ __forceinline__ ProdRec make_rec(const StreamProblem& p, int64_t rowbytes, int64_t GS, bool grouped) {
+  ProdRec r;
+  r.wbase = p.packed - p.row_off * rowbytes;
+  r.sbase = p.scales - (grouped ? p.row_off * GS : 0);
+  r.x = p.x;
+  r.y = p.y;
+  r.ldx = p.ldx;
+  r.ldy = p.ldy;
+  r.roff = (int32_t)p.row_off;
+  r.pend = (int32_t)(p.row_off + p.n);
+  r.yt = p.yt;
+  r.tscale = grouped ? 1.f : f16_bits_to_float(*to_global(p.scales));
+  return r;
+}
+
+// Record index (0..nrec-1) owning a segment row: last record with roff <= row.
+__device__ __forceinline__ int rec_of(const ProdRec* rec, int nrec, int32_t row) {
+  int i = 0;
+  for (int t = 1; t < nrec; ++t) i = rec[t].roff <= row ? t : i;
+  return i;
+}
+
+// seg: segment description; probs: the problem table (nullptr: `single`);
+// wr: {first, last} problem (within the segment) touched by this workgroup.
+template <int XT, int BITS, bool GROUPED, int MR>
+__device__ __forceinline__ void run_segment(const StreamPhase& seg, const StreamProblem* probs,
+                                            const StreamProblem& single, int2 wr, uint8_t* smem,
+                                            uint32_t* sync, uint32_t wait_target, bool coherent) {
+  using CD = Codes<BITS>;
+  using FD = FastDec<XT, BITS>;
+  constexpr int NT = st_threads<MR>();
+  constexpr int NG = NT / 16;
+  constexpr int WPC = 128 / BITS;  // weights per 16-byte chunk
+  constexpr int PC = WPC / 8;      // activation pieces per chunk
+  constexpr int CPG = 128 / WPC;   // chunks per 128-group
+  constexpr int U = ST_U;
+
+  const int tid = threadIdx.x;
+  const int j = tid & 15;
+  const int g = tid >> 4;
+  const int G = gridDim.x;
+  const int64_t N = seg.n_total, k = seg.k;
+  const int32_t C = (int32_t)(k / WPC);
+  const int64_t rowbytes = (int64_t)C * 16;
+  const int32_t GS = (int32_t)(k / 128);
+  const int64_t w = blockIdx.x;
+  const int32_t r0 = (int32_t)(w * N / G), r1 = (int32_t)((w + 1) * N / G);
+  const int32_t R = r1 - r0;
+  if (R == 0) return;  // uniform: this workgroup has no rows in the segment
+  const int nrec = wr.y - wr.x + 1;
+
+  // ---- LDS layout
+  ProdRec* rec = reinterpret_cast<ProdRec*>(smem);
+  const size_t slot_bytes = (size_t)MR * C * (PC * 16 + 8);
+  uint8_t* xbase = smem + (size_t)nrec * sizeof(ProdRec);
+  int32_t* head_row = reinterpret_cast<int32_t*>(xbase + nrec * slot_bytes);
+  int32_t* tail_row = head_row + NG;
+  float* head_val = reinterpret_cast<float*>(tail_row + NG);  // [NG][MR]
+  float* tail_val = head_val + NG * MR;                        // [NG][MR]
+
+  // ---- product records of this workgroup's range
+  for (int i = tid; i < nrec; i += NT) {
+    const StreamProblem& p = probs ? probs[seg.first + wr.x + i] : single;
+    rec[i] = make_rec(p, rowbytes, GS, GROUPED);
+  }
+  if (tid < NG) {
+    head_row[tid] = -1;
+    tail_row[tid] = -1;
+  }
+  __syncthreads();
+
+  // this group's run of 16-chunk steps of rows [r0, r1)
+  const int64_t T16 = (int64_t)R * C / 16;
+  const int64_t s0 = (int64_t)g * T16 / NG, s1 = (int64_t)(g + 1) * T16 / NG;
+  const int64_t nsteps = (T16 + NG - 1) / NG;  // uniform trip count (runs differ by at most 1)
+
+  // ---- producer: weight chunks (and group scales) of the run, ST_U ahead
+  int32_t lrow = r0 + (int32_t)((s0 * 16) / C);
+  int32_t lcol = (int32_t)((s0 * 16) - (int64_t)(lrow - r0) * C);
+  int lpi = rec_of(rec, nrec, lrow < r1 ? lrow : r0);
+  const uint8_t* lw = rec[lpi].wbase;
+  const uint16_t* ls = rec[lpi].sbase;
+  int32_t lend = rec[lpi].pend;
+  int64_t lleft = s1 - s0;
+  // stand-in address past the run: the run's first chunk (or the range's)
+  const int32_t drow = lleft > 0 ? lrow : r0, dcol = lleft > 0 ? lcol : 0;
+  const u4* dummy = reinterpret_cast<const u4*>(lw + (int64_t)drow * rowbytes) + dcol + j;
+  const uint16_t* dsc = GROUPED ? ls + (int64_t)drow * GS + (dcol + j) / CPG : nullptr;
+  auto next_chunk = [&](u4& wv, uint16_t& sv) __attribute__((always_inline)) {
+    const bool ok = lleft > 0;
+    const u4* a = ok ? reinterpret_cast<const u4*>(lw + (int64_t)lrow * rowbytes) + lcol + j : dummy;
+    wv = __builtin_nontemporal_load(to_global(a));
+    if constexpr (GROUPED) {
+      const uint16_t* sa = ok ? ls + (int64_t)lrow * GS + (lcol + j) / CPG : dsc;
+      sv = *to_global(sa);
+    }
+    if (ok) {
+      --lleft;
+      lcol += 16;
+      if (lcol == C) {
+        lcol = 0;
+        if (++lrow == lend && lrow < r1) {
+          ++lpi;
+          lw = rec[lpi].wbase;
+          ls = rec[lpi].sbase;
+          lend = rec[lpi].pend;
+        }
+      }
+    }
+  };
+
+  // ---- activation staging: piece idx -> (record, m, chunk, piece)
+  constexpr int XR = MR == 1 ? 1 : 4;  // pieces per thread per round
+  const int64_t per_slot = (int64_t)MR * C * PC;
+  const int64_t P = nrec * per_slot;
+  auto piece_of = [&](int64_t idx, int& slot, int& m, int64_t& c, int& t) __attribute__((always_inline)) {
+    slot = (int)(idx / per_slot);
+    int64_t rem = idx - (int64_t)slot * per_slot;
+    m = (int)(rem / ((int64_t)C * PC));
+    rem -= (int64_t)m * C * PC;
+    c = rem / PC;
+    t = (int)(rem - c * PC);
+  };
+  u4 xraw[XR];
+  auto load_x_round = [&](int64_t it0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < XR; ++i) {
+      int64_t idx = (it0 + i) * NT + tid;
+      idx = idx < P ? idx : 0;
+      int slot, m, t;
+      int64_t c;
+      piece_of(idx, slot, m, c, t);
+      const uint16_t* xr = rec[slot].x + (int64_t)m * rec[slot].ldx + c * WPC;
+      if constexpr (BITS == 4 || BITS == 8) {
+        xraw[i] = load_x16(xr + 8 * t, coherent);
+      } else {
+        // INT2: the piece's 8 activations are spread over 16 consecutive ones
+        uint16_t v[8];
+#pragma unroll
+        for (int h = 0; h < 8; ++h) {
+          const int pp = 8 * t + h, q = pp % CD::E, e = q / 2 + (q % 2) * (CD::E / 2);
+          v[h] = load_x2(xr + (pp / CD::E) * CD::E + e, coherent);
+        }
+        xraw[i][0] = v[0] | ((uint32_t)v[1] << 16);
+        xraw[i][1] = v[2] | ((uint32_t)v[3] << 16);
+        xraw[i][2] = v[4] | ((uint32_t)v[5] << 16);
+        xraw[i][3] = v[6] | ((uint32_t)v[7] << 16);
+      }
+    }
+  };
+  auto store_x_round = [&](int64_t it0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < XR; ++i) {
+      if ((it0 + i) * NT >= P) break;  // uniform: no live piece in this or later rounds
+      const int64_t idx = (it0 + i) * NT + tid;
+      const bool live = idx < P;
+      int slot, m, t;
+      int64_t c;
+      piece_of(live ? idx : 0, slot, m, c, t);
+      const uint32_t a0 = xraw[i][0], a1 = xraw[i][1], a2 = xraw[i][2], a3 = xraw[i][3];
+      uint16_t v[8];
+      if constexpr (BITS == 4) {  // decoder order (0,4,1,5,2,6,3,7)
+        v[0] = a0 & 0xFFFF; v[1] = a2 & 0xFFFF; v[2] = a0 >> 16; v[3] = a2 >> 16;
+        v[4] = a1 & 0xFFFF; v[5] = a3 & 0xFFFF; v[6] = a1 >> 16; v[7] = a3 >> 16;
+      } else if constexpr (BITS == 8) {  // decoder order (0,2,1,3,4,6,5,7)
+        v[0] = a0 & 0xFFFF; v[1] = a1 & 0xFFFF; v[2] = a0 >> 16; v[3] = a1 >> 16;
+        v[4] = a2 & 0xFFFF; v[5] = a3 & 0xFFFF; v[6] = a2 >> 16; v[7] = a3 >> 16;
+      } else {  // already gathered in decoder order
+        v[0] = a0 & 0xFFFF; v[1] = a0 >> 16; v[2] = a1 & 0xFFFF; v[3] = a1 >> 16;
+        v[4] = a2 & 0xFFFF; v[5] = a2 >> 16; v[6] = a3 & 0xFFFF; v[7] = a3 >> 16;
+      }
+      float se = 0.f, so = 0.f;
+#pragma unroll
+      for (int h = 0; h < 8; ++h) {
+        const int pp = 8 * t + h, q = pp % CD::E, e = q / 2 + (q % 2) * (CD::E / 2);
+        const int kk = (pp / CD::E) * CD::E + e;
+        const float f = x_bits_to_float<XT>(v[h]);
+        if (kk & 1) so += f;
+        else se += f;
+      }
+      uint8_t* sbase = xbase + slot * slot_bytes;
+      if (live) {
+        u4 piece;
+        piece[0] = v[0] | ((uint32_t)v[1] << 16);
+        piece[1] = v[2] | ((uint32_t)v[3] << 16);
+        piece[2] = v[4] | ((uint32_t)v[5] << 16);
+        piece[3] = v[6] | ((uint32_t)v[7] << 16);
+        reinterpret_cast<u4*>(sbase)[((int64_t)m * PC + t) * C + c] = piece;
+      }
+#pragma unroll
+      for (int o = 1; o < PC; o <<= 1) {
+        se += __shfl_xor(se, o, 64);
+        so += __shfl_xor(so, o, 64);
+      }
+      if (live && t == 0)
+        reinterpret_cast<float2*>(sbase + (size_t)MR * C * PC * 16)[(int64_t)m * C + c] = make_float2(se, so);
+    }
+  };
+
+  // ---- prologue: activations (after the dependency wait when there is one)
+  // go out before most of the weights, so they are not queued behind them
+  constexpr int U0 = 2;
+  u4 buf[U];
+  uint16_t sbuf[U];
+  if (!sync) load_x_round(0);
+#pragma unroll
+  for (int u = 0; u < U0; ++u) next_chunk(buf[u], sbuf[u]);
+  if (sync) {
+    // weights and scales do not depend on earlier phases: already in flight
+    if (tid == 0) {
+      uint32_t polls = 0;
+      while (__hip_atomic_load(sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < wait_target) {
+        __builtin_amdgcn_s_sleep(1);
+        if (++polls > (1u << 24)) {  // bounded: record the failure and go on
+          __hip_atomic_fetch_or(sync + 1, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          break;
+        }
+      }
+    }
+    __syncthreads();
+    load_x_round(0);
+  }
+  store_x_round(0);
+#pragma unroll
+  for (int u = U0; u < U; ++u) next_chunk(buf[u], sbuf[u]);
+  for (int64_t it0 = XR; it0 * NT < P; it0 += XR) {
+    load_x_round(it0);
+    store_x_round(it0);
+  }
+  __syncthreads();
+
+  // ---- consumer
+  int32_t row = r0 + (int32_t)((s0 * 16) / C);
+  int32_t col = (int32_t)((s0 * 16) - (int64_t)(row - r0) * C);
+  int pi = rec_of(rec, nrec, row < r1 ? row : r0);
+  int32_t pend = rec[pi].pend;
+  const uint8_t* xs_base = xbase + pi * slot_bytes;
+  bool split_head = col != 0;  // the run starts inside a row
+  float acc[MR];
+#pragma unroll
+  for (int m = 0; m < MR; ++m) acc[m] = 0.f;
+
+  for (int64_t sb = 0; sb < nsteps; sb += U) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const u4 wv = buf[u];
+      const uint16_t sv = sbuf[u];
+      next_chunk(buf[u], sbuf[u]);  // the chunk U steps ahead (or the stand-in)
+      if (s0 + sb + u < s1) {
+        const int32_t c = col + j;
+        const u4* xs = reinterpret_cast<const u4*>(xs_base);
+        const float2* xsum = reinterpret_cast<const float2*>(xs_base + (size_t)MR * C * PC * 16);
+        float sc = 1.f;
+        if constexpr (GROUPED) sc = f16_bits_to_float(sv);
+#pragma unroll
+        for (int m = 0; m < MR; ++m) {
+          // activation pairs of dword dw are pairs [dw*PAIRS, (dw+1)*PAIRS) of
+          // the chunk's pieces; read each 16-byte piece just before first use
+          uint32_t xp[4 * PC];
+          float d = 0.f;
+#pragma unroll
+          for (int dw = 0; dw < 4; ++dw) {
+#pragma unroll
+            for (int t = (dw * CD::PAIRS) / 4; t < ((dw + 1) * CD::PAIRS + 3) / 4; ++t) {
+              if ((dw * CD::PAIRS) % 4 == 0 || t > (dw * CD::PAIRS) / 4) {
+                const u4 pc = xs[((int64_t)m * PC + t) * C + c];
+                xp[4 * t + 0] = pc[0];
+                xp[4 * t + 1] = pc[1];
+                xp[4 * t + 2] = pc[2];
+                xp[4 * t + 3] = pc[3];
+              }
+            }
+            d = FD::dot(wv[dw] ^ CD::SIGNS, xp + dw * CD::PAIRS, d);
+          }
+          const float2 xsm = xsum[(int64_t)m * C + c];
+          const float part = d - FD::BE * xsm.x - FD::BO * xsm.y;
+          if constexpr (GROUPED) acc[m] = __builtin_fmaf(sc, part, acc[m]);
+          else acc[m] += part;
+        }
+        col += 16;
+        if (col == C) {  // the run leaves this row
+          const ProdRec& pr = rec[pi];
+#pragma unroll
+          for (int m = 0; m < MR; ++m) {
+            const float v = row16_sum(acc[m]);
+            acc[m] = 0.f;
+            if (j == 0) {
+              if (split_head) head_val[g * MR + m] = v;
+              else store_y_coherent(pr.y, (int64_t)m * pr.ldy + (row - pr.roff), v * pr.tscale, pr.yt, coherent);
+            }
+          }
+          if (split_head && j == 0) head_row[g] = row;
+          split_head = false;
+          col = 0;
+          if (++row == pend && row < r1) {
+            ++pi;
+            pend = rec[pi].pend;
+            xs_base = xbase + pi * slot_bytes;
+          }
+        }
+      }
+    }
+  }
+  if (s1 > s0 && col != 0) {  // the run ends inside a row
+#pragma unroll
+    for (int m = 0; m < MR; ++m) {
+      const float v = row16_sum(acc[m]);
+      if (j == 0) {
+        if (split_head) head_val[g * MR + m] = v;  // started and ended inside one row
+        else tail_val[g * MR + m] = v;
+      }
+    }
+    if (j == 0) {
+      if (split_head) head_row[g] = row;
+      else tail_row[g] = row;
+    }
+  }
+  __syncthreads();
+
+  // ---- rows split between runs: tail of the group that began the row plus
+  // the heads of the following groups, in group order
+  if (tid < NG && tail_row[tid] >= 0) {
+    const int32_t rr = tail_row[tid];
+    float v[MR];
+#pragma unroll
+    for (int m = 0; m < MR; ++m) v[m] = tail_val[tid * MR + m];
+    for (int g2 = tid + 1; g2 < NG; ++g2) {
+      const bool empty = (int64_t)g2 * T16 / NG == (int64_t)(g2 + 1) * T16 / NG;
+      if (empty) continue;  // groups with empty runs hold no piece of any row
+      if (head_row[g2] != rr) break;
+#pragma unroll
+      for (int m = 0; m < MR; ++m) v[m] += head_val[g2 * MR + m];
+    }
+    const ProdRec& pr = rec[rec_of(rec, nrec, rr)];
+#pragma unroll
+    for (int m = 0; m < MR; ++m)
+      store_y_coherent(pr.y, (int64_t)m * pr.ldy + (rr - pr.roff), v[m] * pr.tscale, pr.yt, coherent);
+  }
+  __syncthreads();  // LDS is reused by the next segment
+}
+
+// variant = (x fp16 ? 0 : 6) + (bits 2/4/8 -> 0/2/4) + (grouped ? 1 : 0)
+__host__ __device__ inline int stream_variant(int xt, int bits, int group) {
+  return (xt == XF16 ? 0 : 6) + (bits == 2 ? 0 : bits == 4 ? 2 : 4) + (group ? 1 : 0);
+}
+constexpr int VAR_ANY = 12;
+
+template <int MR, int V>
+__device__ __forceinline__ void run_variant(const StreamPhase& seg, const StreamProblem* probs,
+                                            const StreamProblem& single, int2 wr, uint8_t* smem,
+                                            uint32_t* sync, uint32_t wt, bool coh) {
+  constexpr int XT = V < 6 ? XF16 : XBF16;
+  constexpr int BITS = (V % 6) / 2 == 0 ? 2 : (V % 6) / 2 == 1 ? 4 : 8;
+  constexpr bool GROUPED = (V % 2) == 1;
+  run_segment<XT, BITS, GROUPED, MR>(seg, probs, single, wr, smem, sync, wt, coh);
+}
+
+template <int MR, int VAR>
+__device__ __forceinline__ void seg_dispatch(const StreamPhase& seg, const StreamProblem* probs,
+                                             const StreamProblem& single, int2 wr, uint8_t* smem,
+                                             uint32_t* sync, uint32_t wt, bool coh) {
+  if constexpr (VAR != VAR_ANY) {
+    run_variant<MR, VAR>(seg, probs, single, wr, smem, sync, wt, coh);
+  } else {
+    switch (stream_variant(seg.xt, seg.bits, seg.group)) {
+      case 0: run_variant<MR, 0>(seg, probs, single, wr, smem, sync, wt, coh); break;
+      case 1: run_variant<MR, 1>(seg, probs, single, wr, smem, sync, wt, coh); break;
+      case 2: run_variant<MR, 2>(seg, probs, single, wr, smem, sync, wt, coh); break;
+      case 3: run_variant<MR, 3>(seg, probs, single, wr, smem, sync, wt, coh); break;
+      case 4: run_variant<MR, 4>(seg, probs, single, wr, smem, sync, wt, coh); break;
+      case 5: run_variant<MR, 5>(seg, probs, single, wr, smem, sync, wt, coh); break;
+      case 6: run_variant<MR, 6>(seg, probs, single, wr, smem, sync, wt, coh); break;
+      case 7: run_variant<MR, 7>(seg, probs, single, wr, smem, sync, wt, coh); break;
+      case 8: run_variant<MR, 8>(seg, probs, single, wr, smem, sync, wt, coh); break;
+      case 9: run_variant<MR, 9>(seg, probs, single, wr, smem, sync, wt, coh); break;
+      case 10: run_variant<MR, 10>(seg, probs, single, wr, smem, sync, wt, coh); break;
+      default: run_variant<MR, 11>(seg, probs, single, wr, smem, sync, wt, coh); break;
+    }
+  }
+}
+
+// Single product: segs == nullptr, `single_seg` and `single_prob` by value.
+// Plan: nseg segments, the problem table, per-(segment, workgroup) problem
+// ranges wranges[s * G + w] = {first, last} (within the segment), and
+// sync = {done counter, error word}. VAR fixes the format (VAR_ANY: a mix).
+template <int MR, int VAR>
+__global__ __launch_bounds__(st_threads<MR>()) void gemv_stream_kernel(
+    const StreamPhase* __restrict__ segs, int nseg, const StreamProblem* __restrict__ probs,
+    const int2* __restrict__ wranges, StreamPhase single_seg, StreamProblem single_prob, uint32_t* sync) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  const uint32_t G = gridDim.x;
+  if (!segs) {
+    seg_dispatch<MR, VAR>(single_seg, nullptr, single_prob, make_int2(0, 0), smem, nullptr, 0, false);
+    return;
+  }
+  uint32_t waits = 0;
+  for (int s = 0; s < nseg; ++s) {
+    const StreamPhase seg = segs[s];
+    uint32_t* ws = nullptr;
+    if (seg.wait) {
+      // this workgroup's outputs of the previous phase are stored
+      // (agent-coherent): wait for them to complete, count the workgroup done
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      if (threadIdx.x == 0) __hip_atomic_fetch_add(sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      ++waits;
+      ws = sync;
+    }
+    const int2 wr = wranges[(int64_t)s * G + blockIdx.x];
+    seg_dispatch<MR, VAR>(seg, probs, single_prob, wr, smem, ws, waits * G, true);
+  }
+}
+
+template <int MR, int VAR>
+static const void* stream_fn() {
+  return reinterpret_cast<const void*>(&gemv_stream_kernel<MR, VAR>);
+}
+
+template <int MR>
+static const void* stream_fn_var(int var) {
+  switch (var) {
+    case 0: return stream_fn<MR, 0>();
+    case 1: return stream_fn<MR, 1>();
+    case 2: return stream_fn<MR, 2>();
+    case 3: return stream_fn<MR, 3>();
+    case 4: return stream_fn<MR, 4>();
+    case 5: return stream_fn<MR, 5>();
+    case 6: return stream_fn<MR, 6>();
+    case 7: return stream_fn<MR, 7>();
+    case 8: return stream_fn<MR, 8>();
+    case 9: return stream_fn<MR, 9>();
+    case 10: return stream_fn<MR, 10>();
+    case 11: return stream_fn<MR, 11>();
+    default: return stream_fn<MR, VAR_ANY>();
+  }
+}
+
+// kernels for MR activation rows, one translation unit each (zq_stream_m*.hip)
+const void* stream_kernel_m1(int var);
+const void* stream_kernel_m2(int var);
+const void* stream_kernel_m3(int var);
+const void* stream_kernel_m4(int var);
+
+}  // namespace zq

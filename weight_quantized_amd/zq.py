@@ -21,6 +21,7 @@ _DT = {torch.int8: I8, torch.float16: F16, torch.bfloat16: BF16, torch.float32: 
 
 # every exported symbol of include/zq.h
 SYMBOLS = ("zq_packed_bytes", "zq_num_scales", "zq_pack", "zq_unpack", "zq_gemv", "zq_gemm",
+           "zq_plan_create", "zq_plan_run", "zq_plan_check", "zq_plan_destroy",
            "zq_status_string", "zq_last_error")
 
 
@@ -33,6 +34,12 @@ class ZqError(RuntimeError):
 class _Weight(ctypes.Structure):
     _fields_ = [("bits", ctypes.c_int32), ("group", ctypes.c_int32), ("n", ctypes.c_int64),
                 ("k", ctypes.c_int64), ("packed", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+
+
+class _Problem(ctypes.Structure):
+    _fields_ = [("w", _Weight), ("x", ctypes.c_void_p), ("x_dtype", ctypes.c_int32),
+                ("ldx", ctypes.c_int64), ("y", ctypes.c_void_p), ("y_dtype", ctypes.c_int32),
+                ("ldy", ctypes.c_int64), ("phase", ctypes.c_int32)]
 
 
 _lib = None
@@ -56,6 +63,12 @@ def lib() -> ctypes.CDLL:
         L.zq_gemv.argtypes = [wp, vp, i32, vp, i32, vp]
         L.zq_gemm.argtypes = [wp, vp, i32, i64, i64, vp, i32, i64, vp]
         for f in ("zq_pack", "zq_unpack", "zq_gemv", "zq_gemm"):
+            getattr(L, f).restype = i32
+        L.zq_plan_create.argtypes = [ctypes.POINTER(_Problem), i32, i64, ctypes.POINTER(vp)]
+        L.zq_plan_run.argtypes = [vp, vp]
+        L.zq_plan_check.argtypes = [vp]
+        L.zq_plan_destroy.argtypes = [vp]
+        for f in ("zq_plan_create", "zq_plan_run", "zq_plan_check", "zq_plan_destroy"):
             getattr(L, f).restype = i32
         L.zq_status_string.argtypes = [i32]
         L.zq_status_string.restype = ctypes.c_char_p
@@ -156,3 +169,39 @@ def gemm_raw(W: ZqWeight, x_ptr: int, x_dtype: int, m: int, ldx: int, y_ptr: int
     d = W.desc()
     _check(lib().zq_gemm(ctypes.byref(d), x_ptr, x_dtype, m, ldx, y_ptr, y_dtype, ldy, stream),
            "zq_gemm")
+
+
+class Plan:
+    """Many products in one resident launch (zq_plan_*). `problems` is a list of
+    (ZqWeight, X [m, k], Y [m, n], phase); phases must not decrease."""
+
+    def __init__(self, problems):
+        self._keep = problems  # the plan reads these buffers at every run
+        m = problems[0][1].shape[0] if problems[0][1].dim() == 2 else 1
+        arr = (_Problem * len(problems))()
+        for i, (W, X, Y, phase) in enumerate(problems):
+            X2 = X if X.dim() == 2 else X.view(1, -1)
+            Y2 = Y if Y.dim() == 2 else Y.view(1, -1)
+            arr[i] = _Problem(W.desc(), _ptr(X2), _DT.get(X2.dtype, -1), X2.stride(0), _ptr(Y2),
+                              _DT.get(Y2.dtype, -1), Y2.stride(0), phase)
+        h = ctypes.c_void_p()
+        _check(lib().zq_plan_create(arr, len(problems), m, ctypes.byref(h)), "zq_plan_create")
+        self._h = h
+        self.device = problems[0][1].device
+
+    def run(self) -> None:
+        _check(lib().zq_plan_run(self._h, torch.cuda.current_stream(self.device).cuda_stream), "zq_plan_run")
+
+    def check(self) -> None:
+        _check(lib().zq_plan_check(self._h), "zq_plan_check")
+
+    def close(self) -> None:
+        if self._h:
+            _check(lib().zq_plan_destroy(self._h), "zq_plan_destroy")
+            self._h = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
