@@ -61,20 +61,24 @@ struct FastDec {
                               : (XT == XF16 && BITS == 8) ? 1152.f
                                                           : Decoder<XT, BITS>::BIAS;
   static constexpr float BO = (XT == XF16 && BITS == 4) ? 72.f : BE;
+  // dot of one raw packed dword (codes not yet sign-flipped) with its
+  // activation pairs. The sign flip is folded into the masking:
+  // ((v ^ S) & M) | O == (v & M) ^ ((S & M) ^ O), one v_bitop3 per pair.
   static __device__ __forceinline__ float dot(uint32_t v, const uint32_t* xq, float d) {
     if constexpr (XT == XF16 && BITS == 4) {
       const uint32_t t = v >> 8;
-      d = dot2<XF16>((v & 0x000F000Fu) | 0x64006400u, xq[0], d);
-      d = dot2<XF16>((v & 0x00F000F0u) | 0x54005400u, xq[1], d);
-      d = dot2<XF16>((t & 0x000F000Fu) | 0x64006400u, xq[2], d);
-      d = dot2<XF16>((t & 0x00F000F0u) | 0x54005400u, xq[3], d);
+      d = dot2<XF16>((v & 0x000F000Fu) ^ (0x00080008u ^ 0x64006400u), xq[0], d);
+      d = dot2<XF16>((v & 0x00F000F0u) ^ (0x00800080u ^ 0x54005400u), xq[1], d);
+      d = dot2<XF16>((t & 0x000F000Fu) ^ (0x00080008u ^ 0x64006400u), xq[2], d);
+      d = dot2<XF16>((t & 0x00F000F0u) ^ (0x00800080u ^ 0x54005400u), xq[3], d);
       return d;
     } else if constexpr (XT == XF16 && BITS == 8) {
-      d = dot2<XF16>((v & 0x00FF00FFu) | 0x64006400u, xq[0], d);
-      d = dot2<XF16>(((v >> 8) & 0x00FF00FFu) | 0x64006400u, xq[1], d);
+      d = dot2<XF16>((v & 0x00FF00FFu) ^ (0x00800080u ^ 0x64006400u), xq[0], d);
+      d = dot2<XF16>(((v >> 8) & 0x00FF00FFu) ^ (0x00800080u ^ 0x64006400u), xq[1], d);
       return d;
     } else {
       using D = Decoder<XT, BITS>;
+      v ^= Codes<BITS>::SIGNS;
       [&]<int... I>(std::integer_sequence<int, I...>) {
         ((d = dot2<XT>(D::template pair<I>(v), xq[I], d)), ...);
       }(std::make_integer_sequence<int, Codes<BITS>::PAIRS>{});
@@ -99,8 +103,8 @@ static_assert(sizeof(ProdRec) == 64, "LDS record layout");
 // LDS bytes of one workgroup's view of a segment touching nrec products
 __host__ __device__ inline size_t stream_seg_lds(int bits, int64_t mr, int64_t k, int nrec) {
   const int64_t wpc = 128 / bits, pc = wpc / 8, C = k / wpc;
-  const int ng = mr == 1 ? 64 : 32;
-  return (size_t)nrec * 64 + (size_t)nrec * mr * C * (pc * 16 + 8) + (size_t)ng * (8 + 8 * mr);
+  const int nw = mr == 1 ? 16 : 8;  // waves
+  return (size_t)nrec * 64 + (size_t)nrec * mr * C * (pc + 1) * 16 + (size_t)nw * (8 + 32 * mr);
 }
 
 // 16 bytes of activations, optionally with agent-coherent loads (the buffer
@@ -157,6 +161,12 @@ __device__ __forceinline__ int rec_of(const ProdRec* rec, int nrec, int32_t row)
 
 // seg: segment description; probs: the problem table (nullptr: `single`);
 // wr: {first, last} problem (within the segment) touched by this workgroup.
+//
+// Work split inside the workgroup: rows [r0, r1) form quads of 4 rows; a
+// quad-step is one 16-chunk column block of a quad (4 x 256 contiguous-row
+// bytes). Each wave takes an equal, contiguous run of quad-steps (quad-major),
+// its 16-lane group q4 handling row 4*quad + q4, so all four groups of a wave
+// cross row ends together: every branch of the main loop is wave-uniform.
 template <int XT, int BITS, bool GROUPED, int MR>
 __device__ __forceinline__ void run_segment(const StreamPhase& seg, const StreamProblem* probs,
                                             const StreamProblem& single, int2 wr, uint8_t* smem,
@@ -164,18 +174,24 @@ __device__ __forceinline__ void run_segment(const StreamPhase& seg, const Stream
   using CD = Codes<BITS>;
   using FD = FastDec<XT, BITS>;
   constexpr int NT = st_threads<MR>();
-  constexpr int NG = NT / 16;
+  constexpr int NW = NT / 64;      // waves
   constexpr int WPC = 128 / BITS;  // weights per 16-byte chunk
   constexpr int PC = WPC / 8;      // activation pieces per chunk
   constexpr int CPG = 128 / WPC;   // chunks per 128-group
+  constexpr int SPS = 16 / CPG;    // scale entries per step
   constexpr int U = ST_U;
 
   const int tid = threadIdx.x;
-  const int j = tid & 15;
-  const int g = tid >> 4;
+  const int lane = tid & 63;
+  const int j = lane & 15;
+  const int q4 = lane >> 4;
+  // wave index as a scalar: the run bookkeeping below is wave-uniform and
+  // then lives in SGPRs with scalar branches
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int G = gridDim.x;
   const int64_t N = seg.n_total, k = seg.k;
   const int32_t C = (int32_t)(k / WPC);
+  const int32_t CB = C / 16;  // column blocks (steps) per row
   const int64_t rowbytes = (int64_t)C * 16;
   const int32_t GS = (int32_t)(k / 128);
   const int64_t w = blockIdx.x;
@@ -186,61 +202,74 @@ __device__ __forceinline__ void run_segment(const StreamPhase& seg, const Stream
 
   // ---- LDS layout
   ProdRec* rec = reinterpret_cast<ProdRec*>(smem);
-  const size_t slot_bytes = (size_t)MR * C * (PC * 16 + 8);
+  // activation slot of one product: blocks of 16 chunks (one step); block b
+  // holds, for each row m, PC rows of 16 pieces (piece t of chunk 16b+jj at
+  // (m*(PC+1) + t)*256 + jj*16) and then 16 float4 sums (even, odd, 0, 0), so
+  // a lane reads everything of its chunk at constant offsets from one pointer
+  constexpr int BS = MR * (PC + 1) * 256;  // bytes per block
+  const size_t slot_bytes = (size_t)CB * BS;
   uint8_t* xbase = smem + (size_t)nrec * sizeof(ProdRec);
-  int32_t* head_row = reinterpret_cast<int32_t*>(xbase + nrec * slot_bytes);
-  int32_t* tail_row = head_row + NG;
-  float* head_val = reinterpret_cast<float*>(tail_row + NG);  // [NG][MR]
-  float* tail_val = head_val + NG * MR;                        // [NG][MR]
+  int32_t* head_q = reinterpret_cast<int32_t*>(xbase + nrec * slot_bytes);  // [NW] quad of the head
+  int32_t* tail_q = head_q + NW;                                           // [NW]
+  float* head_val = reinterpret_cast<float*>(tail_q + NW);                 // [NW][4][MR]
+  float* tail_val = head_val + NW * 4 * MR;                                // [NW][4][MR]
 
   // ---- product records of this workgroup's range
   for (int i = tid; i < nrec; i += NT) {
     const StreamProblem& p = probs ? probs[seg.first + wr.x + i] : single;
     rec[i] = make_rec(p, rowbytes, GS, GROUPED);
   }
-  if (tid < NG) {
-    head_row[tid] = -1;
-    tail_row[tid] = -1;
+  if (tid < NW) {
+    head_q[tid] = -1;
+    tail_q[tid] = -1;
   }
   __syncthreads();
 
-  // this group's run of 16-chunk steps of rows [r0, r1)
-  const int64_t T16 = (int64_t)R * C / 16;
-  const int64_t s0 = (int64_t)g * T16 / NG, s1 = (int64_t)(g + 1) * T16 / NG;
-  const int64_t nsteps = (T16 + NG - 1) / NG;  // uniform trip count (runs differ by at most 1)
+  // this wave's run of quad-steps
+  const int32_t NQ = (R + 3) / 4;
+  const int64_t T = (int64_t)NQ * CB;
+  const int64_t s0 = (int64_t)wv * T / NW, s1 = (int64_t)(wv + 1) * T / NW;
+  const int64_t nsteps = (T + NW - 1) / NW;  // uniform trip count (runs differ by at most 1)
 
-  // ---- producer: weight chunks (and group scales) of the run, ST_U ahead
-  int32_t lrow = r0 + (int32_t)((s0 * 16) / C);
-  int32_t lcol = (int32_t)((s0 * 16) - (int64_t)(lrow - r0) * C);
-  int lpi = rec_of(rec, nrec, lrow < r1 ? lrow : r0);
-  const uint8_t* lw = rec[lpi].wbase;
-  const uint16_t* ls = rec[lpi].sbase;
-  int32_t lend = rec[lpi].pend;
-  int64_t lleft = s1 - s0;
-  // stand-in address past the run: the run's first chunk (or the range's)
-  const int32_t drow = lleft > 0 ? lrow : r0, dcol = lleft > 0 ? lcol : 0;
-  const u4* dummy = reinterpret_cast<const u4*>(lw + (int64_t)drow * rowbytes) + dcol + j;
-  const uint16_t* dsc = GROUPED ? ls + (int64_t)drow * GS + (dcol + j) / CPG : nullptr;
-  auto next_chunk = [&](u4& wv, uint16_t& sv) __attribute__((always_inline)) {
-    const bool ok = lleft > 0;
-    const u4* a = ok ? reinterpret_cast<const u4*>(lw + (int64_t)lrow * rowbytes) + lcol + j : dummy;
-    wv = __builtin_nontemporal_load(to_global(a));
-    if constexpr (GROUPED) {
-      const uint16_t* sa = ok ? ls + (int64_t)lrow * GS + (lcol + j) / CPG : dsc;
-      sv = *to_global(sa);
-    }
-    if (ok) {
+  // row of this lane in quad qd (rows past the range re-read the last row)
+  auto quad_row = [&](int32_t qd) __attribute__((always_inline)) -> int32_t {
+    const int32_t rr = r0 + 4 * qd + q4;
+    return rr < r1 ? rr : r1 - 1;
+  };
+  auto rec_at = [&](int32_t row) __attribute__((always_inline)) -> int {
+    return rec_of(rec, nrec, row);
+  };
+
+  // ---- producer: weight chunks (and group scales) of the run, ST_U ahead.
+  // Within a quad row the lane's pointers advance by one step (256 bytes,
+  // 16/CPG scales); at a block wrap they move to the lane's row of the next
+  // quad. At the end of its run a wave keeps re-reading its last chunks
+  // (cached); the consumer discards those.
+  int32_t lq = (int32_t)(s0 / CB), lb = (int32_t)(s0 % CB);
+  if (s1 == s0) { lq = 0; lb = 0; }  // empty run: a valid stand-in address
+  int32_t lrow = quad_row(lq);
+  int lpi = rec_at(lrow);
+  const u4* lptr = reinterpret_cast<const u4*>(rec[lpi].wbase + (int64_t)lrow * rowbytes) + lb * 16 + j;
+  const uint16_t* lsp = GROUPED ? rec[lpi].sbase + (int64_t)lrow * GS + lb * SPS + j / CPG : nullptr;
+  int32_t lleft = (int32_t)(s1 - s0);  // quad-steps not yet requested
+  auto next_chunk = [&](u4& wvv, uint16_t& sv) __attribute__((always_inline)) {
+    wvv = __builtin_nontemporal_load(to_global(lptr));
+    if constexpr (GROUPED) sv = *to_global(lsp);
+    if (lleft > 1) {  // wave-uniform
       --lleft;
-      lcol += 16;
-      if (lcol == C) {
-        lcol = 0;
-        if (++lrow == lend && lrow < r1) {
-          ++lpi;
-          lw = rec[lpi].wbase;
-          ls = rec[lpi].sbase;
-          lend = rec[lpi].pend;
-        }
+      if (++lb == CB) {
+        lb = 0;
+        ++lq;
+        lrow = quad_row(lq);
+        while (lrow >= rec[lpi].pend) ++lpi;
+        lptr = reinterpret_cast<const u4*>(rec[lpi].wbase + (int64_t)lrow * rowbytes) + j;
+        if constexpr (GROUPED) lsp = rec[lpi].sbase + (int64_t)lrow * GS + j / CPG;
+      } else {
+        lptr += 16;
+        if constexpr (GROUPED) lsp += SPS;
       }
+    } else {
+      lleft = 0;
     }
   };
 
@@ -313,14 +342,14 @@ __device__ __forceinline__ void run_segment(const StreamPhase& seg, const Stream
         if (kk & 1) so += f;
         else se += f;
       }
-      uint8_t* sbase = xbase + slot * slot_bytes;
+      uint8_t* blk = xbase + slot * slot_bytes + (size_t)(c / 16) * BS + (c % 16) * 16;
       if (live) {
         u4 piece;
         piece[0] = v[0] | ((uint32_t)v[1] << 16);
         piece[1] = v[2] | ((uint32_t)v[3] << 16);
         piece[2] = v[4] | ((uint32_t)v[5] << 16);
         piece[3] = v[6] | ((uint32_t)v[7] << 16);
-        reinterpret_cast<u4*>(sbase)[((int64_t)m * PC + t) * C + c] = piece;
+        *reinterpret_cast<u4*>(blk + (m * (PC + 1) + t) * 256) = piece;
       }
 #pragma unroll
       for (int o = 1; o < PC; o <<= 1) {
@@ -328,7 +357,7 @@ __device__ __forceinline__ void run_segment(const StreamPhase& seg, const Stream
         so += __shfl_xor(so, o, 64);
       }
       if (live && t == 0)
-        reinterpret_cast<float2*>(sbase + (size_t)MR * C * PC * 16)[(int64_t)m * C + c] = make_float2(se, so);
+        *reinterpret_cast<f4*>(blk + (m * (PC + 1) + PC) * 256) = f4{se, so, 0.f, 0.f};
     }
   };
 
@@ -365,12 +394,13 @@ __device__ __forceinline__ void run_segment(const StreamPhase& seg, const Stream
   __syncthreads();
 
   // ---- consumer
-  int32_t row = r0 + (int32_t)((s0 * 16) / C);
-  int32_t col = (int32_t)((s0 * 16) - (int64_t)(row - r0) * C);
-  int pi = rec_of(rec, nrec, row < r1 ? row : r0);
-  int32_t pend = rec[pi].pend;
-  const uint8_t* xs_base = xbase + pi * slot_bytes;
-  bool split_head = col != 0;  // the run starts inside a row
+  int32_t cq = (int32_t)(s0 / CB), cb = (int32_t)(s0 % CB);
+  int32_t row = quad_row(cq);
+  bool row_ok = r0 + 4 * cq + q4 < r1;
+  int pi = rec_at(row);
+  const uint8_t* slot0 = xbase + pi * slot_bytes + j * 16;  // block 0 of this product, lane j
+  const uint8_t* xp8 = slot0 + (size_t)cb * BS;            // block of the current step
+  bool split_head = cb != 0;  // the run starts inside a quad
   float acc[MR];
 #pragma unroll
   for (int m = 0; m < MR; ++m) acc[m] = 0.f;
@@ -378,13 +408,10 @@ __device__ __forceinline__ void run_segment(const StreamPhase& seg, const Stream
   for (int64_t sb = 0; sb < nsteps; sb += U) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const u4 wv = buf[u];
+      const u4 wq = buf[u];
       const uint16_t sv = sbuf[u];
       next_chunk(buf[u], sbuf[u]);  // the chunk U steps ahead (or the stand-in)
-      if (s0 + sb + u < s1) {
-        const int32_t c = col + j;
-        const u4* xs = reinterpret_cast<const u4*>(xs_base);
-        const float2* xsum = reinterpret_cast<const float2*>(xs_base + (size_t)MR * C * PC * 16);
+      if (s0 + sb + u < s1) {       // wave-uniform
         float sc = 1.f;
         if constexpr (GROUPED) sc = f16_bits_to_float(sv);
 #pragma unroll
@@ -398,78 +425,86 @@ __device__ __forceinline__ void run_segment(const StreamPhase& seg, const Stream
 #pragma unroll
             for (int t = (dw * CD::PAIRS) / 4; t < ((dw + 1) * CD::PAIRS + 3) / 4; ++t) {
               if ((dw * CD::PAIRS) % 4 == 0 || t > (dw * CD::PAIRS) / 4) {
-                const u4 pc = xs[((int64_t)m * PC + t) * C + c];
+                const u4 pc = *reinterpret_cast<const u4*>(xp8 + (m * (PC + 1) + t) * 256);
                 xp[4 * t + 0] = pc[0];
                 xp[4 * t + 1] = pc[1];
                 xp[4 * t + 2] = pc[2];
                 xp[4 * t + 3] = pc[3];
               }
             }
-            d = FD::dot(wv[dw] ^ CD::SIGNS, xp + dw * CD::PAIRS, d);
+            d = FD::dot(wq[dw], xp + dw * CD::PAIRS, d);
           }
-          const float2 xsm = xsum[(int64_t)m * C + c];
-          const float part = d - FD::BE * xsm.x - FD::BO * xsm.y;
+          const f4 xsm = *reinterpret_cast<const f4*>(xp8 + (m * (PC + 1) + PC) * 256);
+          const float part = d - FD::BE * xsm[0] - FD::BO * xsm[1];
           if constexpr (GROUPED) acc[m] = __builtin_fmaf(sc, part, acc[m]);
           else acc[m] += part;
         }
-        col += 16;
-        if (col == C) {  // the run leaves this row
+        xp8 += BS;
+        if (++cb == CB) {  // wave-uniform: the four rows of this quad end
           const ProdRec& pr = rec[pi];
 #pragma unroll
           for (int m = 0; m < MR; ++m) {
             const float v = row16_sum(acc[m]);
             acc[m] = 0.f;
             if (j == 0) {
-              if (split_head) head_val[g * MR + m] = v;
-              else store_y_coherent(pr.y, (int64_t)m * pr.ldy + (row - pr.roff), v * pr.tscale, pr.yt, coherent);
+              if (split_head) head_val[(wv * 4 + q4) * MR + m] = v;
+              else if (row_ok)
+                store_y_coherent(pr.y, (int64_t)m * pr.ldy + (row - pr.roff), v * pr.tscale, pr.yt, coherent);
             }
           }
-          if (split_head && j == 0) head_row[g] = row;
+          if (split_head && lane == 0) head_q[wv] = cq;
           split_head = false;
-          col = 0;
-          if (++row == pend && row < r1) {
-            ++pi;
-            pend = rec[pi].pend;
-            xs_base = xbase + pi * slot_bytes;
+          cb = 0;
+          ++cq;
+          row = quad_row(cq);
+          row_ok = r0 + 4 * cq + q4 < r1;
+          if (row >= rec[pi].pend) {
+            while (row >= rec[pi].pend) ++pi;
+            slot0 = xbase + pi * slot_bytes + j * 16;
           }
+          xp8 = slot0;
         }
       }
     }
   }
-  if (s1 > s0 && col != 0) {  // the run ends inside a row
+  if (s1 > s0 && cb != 0) {  // the run ends inside a quad
 #pragma unroll
     for (int m = 0; m < MR; ++m) {
       const float v = row16_sum(acc[m]);
       if (j == 0) {
-        if (split_head) head_val[g * MR + m] = v;  // started and ended inside one row
-        else tail_val[g * MR + m] = v;
+        if (split_head) head_val[(wv * 4 + q4) * MR + m] = v;  // started and ended in one quad
+        else tail_val[(wv * 4 + q4) * MR + m] = v;
       }
     }
-    if (j == 0) {
-      if (split_head) head_row[g] = row;
-      else tail_row[g] = row;
+    if (lane == 0) {
+      if (split_head) head_q[wv] = cq;
+      else tail_q[wv] = cq;
     }
   }
   __syncthreads();
 
-  // ---- rows split between runs: tail of the group that began the row plus
-  // the heads of the following groups, in group order
-  if (tid < NG && tail_row[tid] >= 0) {
-    const int32_t rr = tail_row[tid];
-    float v[MR];
+  // ---- quads split between runs: tail of the wave that began the quad plus
+  // the heads of the following waves, in wave order; one thread per row
+  if (tid < NW * 4) {
+    const int w0 = tid >> 2, r4 = tid & 3;
+    const int32_t qd = tail_q[w0];
+    const int32_t rr = r0 + 4 * qd + r4;
+    if (qd >= 0 && rr < r1) {
+      float v[MR];
 #pragma unroll
-    for (int m = 0; m < MR; ++m) v[m] = tail_val[tid * MR + m];
-    for (int g2 = tid + 1; g2 < NG; ++g2) {
-      const bool empty = (int64_t)g2 * T16 / NG == (int64_t)(g2 + 1) * T16 / NG;
-      if (empty) continue;  // groups with empty runs hold no piece of any row
-      if (head_row[g2] != rr) break;
+      for (int m = 0; m < MR; ++m) v[m] = tail_val[(w0 * 4 + r4) * MR + m];
+      for (int w2 = w0 + 1; w2 < NW; ++w2) {
+        const bool empty = (int64_t)w2 * T / NW == (int64_t)(w2 + 1) * T / NW;
+        if (empty) continue;  // waves with empty runs hold no piece of any quad
+        if (head_q[w2] != qd) break;
 #pragma unroll
-      for (int m = 0; m < MR; ++m) v[m] += head_val[g2 * MR + m];
+        for (int m = 0; m < MR; ++m) v[m] += head_val[(w2 * 4 + r4) * MR + m];
+      }
+      const ProdRec& pr = rec[rec_at(rr)];
+#pragma unroll
+      for (int m = 0; m < MR; ++m)
+        store_y_coherent(pr.y, (int64_t)m * pr.ldy + (rr - pr.roff), v[m] * pr.tscale, pr.yt, coherent);
     }
-    const ProdRec& pr = rec[rec_of(rec, nrec, rr)];
-#pragma unroll
-    for (int m = 0; m < MR; ++m)
-      store_y_coherent(pr.y, (int64_t)m * pr.ldy + (rr - pr.roff), v[m] * pr.tscale, pr.yt, coherent);
   }
   __syncthreads();  // LDS is reused by the next segment
 }
