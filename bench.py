@@ -3,9 +3,10 @@
 
 Default workload (one "step" = one decode token through a Qwen2.5-7B-shaped
 stack): 28 layers x 7 projections (q, k, v, o, gate, up, down), each its own
-INT4 group-128 weight, M = 1, fp16 activations, fp32 outputs; 196 launches of
-zq_gemm per step, replayed as one HIP graph. All inputs are synthetic, seeded
-and resident in HBM before timing starts.
+INT4 group-128 weight and its own activation row, M = 1, fp16 activations,
+fp32 outputs; the 196 products of a step run as one plan (one resident
+launch). All inputs are synthetic, seeded and resident in HBM before timing
+starts.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config qwen7b-decode]
 
@@ -15,6 +16,8 @@ Prints one JSON line. Other workloads (--config):
   qwen32b-decode       64 layers of Qwen2.5-32B projection shapes, M = 1
   qwen7b-prefill       7B stack, bits per layer from {2,4,8}, per-tensor scales,
                        M = 2048 bf16 tokens (MFMA-bound: TFLOP/s)
+  hbm-copy             a plain 1 GiB device-to-device copy (torch), the
+                       measured copy ceiling and the byte-counter calibration
 """
 from __future__ import annotations
 
@@ -31,6 +34,28 @@ import numpy as np
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, 8 TB/s
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, 2.5 PFLOP/s
 METRIC = "weight GB/s and % HBM roofline (M=1 INT4 GEMV); decode tok/s equiv for 7B/32B stacks"
+SETTLE_S = 0.3               # untimed streaming before the warmup steps: clocks ramp over ~30 ms
+
+# HBM bytes per launch of the plan kernel from two rocprofv3 --pmc runs
+# (FETCH_SIZE, then WRITE_SIZE), each scaled by what that counter reads for a
+# 1 GiB device copy (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0); the summary and the
+# commands are in profiles/gemv_stream_qwen7b_decode_m1.md. A figure holds only
+# for the kernel sources it was taken with (sha256 of KERNEL_SOURCES, first 16
+# hex digits); for any other source the bench reports traffic as null.
+KERNEL_SOURCES = ("weight_quantized_amd/csrc/zq_stream_impl.hpp", "weight_quantized_amd/csrc/zq_device.hpp",
+                  "weight_quantized_amd/csrc/zq_internal.hpp", "weight_quantized_amd/csrc/zq_stream_m1.hip",
+                  "weight_quantized_amd/csrc/zq_stream.hip")
+TRAFFIC = {("qwen7b-decode", 1, "plan", "independent"): (3400732665, "e57cd12d3603b261")}
+
+
+def kernel_source_hash() -> str:
+    import hashlib
+    h = hashlib.sha256()
+    root = os.path.dirname(os.path.abspath(__file__))
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(root, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def parse():
@@ -39,14 +64,16 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", default="qwen7b-decode",
-                   choices=["gemv-512", "qwen7b-decode", "qwen7b-batch", "qwen32b-decode", "qwen7b-prefill"])
+                   choices=["gemv-512", "qwen7b-decode", "qwen7b-batch", "qwen32b-decode", "qwen7b-prefill",
+                            "hbm-copy"])
     p.add_argument("--m", type=int, default=None, help="activation rows (qwen7b-batch)")
     p.add_argument("--launch", default=None, choices=["plan", "graph", "eager"],
                    help="plan: one resident launch per step (m <= 4, the default there); "
                         "graph: the per-projection launches replayed as a HIP graph")
-    p.add_argument("--order", default="chained", choices=["chained", "independent"],
-                   help="plan phases: chained = q,k,v -> o -> gate,up -> down per layer (each phase "
-                        "waits for the previous one); independent = every product of the step at once")
+    p.add_argument("--order", default="independent", choices=["chained", "independent"],
+                   help="plan phases: independent = every product of the step at once (each has its "
+                        "own activations); chained = q,k,v -> o -> gate,up -> down per layer, each "
+                        "phase waiting for the previous one, as a decoder's data flow would")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--layers", type=int, default=None, help="override the layer count (profiling)")
     return p.parse_args()
@@ -195,6 +222,30 @@ def cpu_baseline(stack: Stack, torch, synth, budget_s: float = 12.0):
                       f"m={xrows} of {stack.m}), {cpu_seconds:.1f} CPU-s over {wall:.2f} s wall"}
 
 
+def copy_bench(a, torch):
+    """dst.copy_(src) of 1 GiB: read 1 GiB + write 1 GiB per step."""
+    nbytes = 1 << 30
+    src = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0").random_(0, 256)
+    dst = torch.empty_like(src)
+    for _ in range(a.warmup):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(a.steps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / a.steps
+    gbs = 2 * nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({"metric": "device copy GB/s (read + write)", "value": round(gbs, 1), "unit": "GB/s",
+                      "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 5),
+                      "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "u8",
+                      "data": "synthetic", "config": {"workload": "1 GiB device-to-device copy",
+                                                      "bytes_read": nbytes, "bytes_written": nbytes}}),
+          flush=True)
+
+
 def main():
     a = parse()
     if a.gpus != 1:
@@ -204,6 +255,9 @@ def main():
     import torch
     from weight_quantized_amd import synth, zq
     zq.lib()
+    if a.config == "hbm-copy":
+        copy_bench(a, torch)
+        return
     if a.config == "qwen7b-prefill" and a.steps == 50:
         a.steps = 10
     stack = Stack(a.config, a.m, a.layers, torch, zq, synth)
@@ -228,6 +282,10 @@ def main():
         run = graph.replay
     else:
         run = stack.step
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < SETTLE_S:
+        run()
+        torch.cuda.synchronize()
     for _ in range(a.warmup):
         run()
     torch.cuda.synchronize()
@@ -281,12 +339,15 @@ def main():
     else:
         gbs = stack.weight_bytes / (ms * 1e-3) / 1e9
         kern_gbs = (stack.weight_bytes / launches) / (avg_launch_ms * 1e-3) / 1e9
+        tr = TRAFFIC.get((a.config, stack.m, a.launch, a.order if a.launch == "plan" else "stream"))
+        traffic = tr[0] if tr and a.layers is None and tr[1] == kernel_source_hash() else None
         out.update({"value": round(gbs, 1), "unit": "GB/s", "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                     "us_per_layer": round(per_layer_us, 3),
                     "tok_s_equiv": round(stack.m / (ms * 1e-3), 1),
                     "roofline": {"bound": "hbm", "achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS,
                                  "unit": "GB/s", "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
-                                 "traffic": None}})
+                                 "traffic": traffic},
+                    "roofline_bytes_per_launch": stack.weight_bytes // launches})
     out["config"] = {"workload": {
         "gemv-512": "single 512x512 INT4 GEMV, per-tensor fp16 scale 0.02, M=1, fp16 x",
         "qwen7b-decode": "Qwen2.5-7B-shaped decode stack: 28 layers x 7 projections, M=1, INT4 group-128, fp16 x",
@@ -295,8 +356,9 @@ def main():
         "qwen7b-prefill": "Qwen2.5-7B-shaped prefill stack, per-layer INT2/INT4/INT8, per-tensor scale, M=2048, bf16 x",
     }[a.config], "layers": stack.layers, "m": stack.m,
         "weight_bytes_per_step": stack.weight_bytes, "launch": a.launch, "order": a.order if a.launch == "plan" else "stream",
-        "launches_per_step": 2 if a.launch == "plan" else len(stack.launches),
-        "wall_ms_per_step": round(wall_ms, 5), "avg_kernel_us": round(avg_launch_ms * 1e3, 3)}
+        "launches_per_step": 1 if a.launch == "plan" else len(stack.launches),
+        "wall_ms_per_step": round(wall_ms, 5), "avg_kernel_us": round(avg_launch_ms * 1e3, 3),
+        "settle_s": SETTLE_S}
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(stack, torch, synth)
     print(json.dumps(out), flush=True)

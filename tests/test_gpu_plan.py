@@ -138,3 +138,28 @@ def test_plan_validation():
     with pytest.raises(zq.ZqError) as e:
         zq.Plan([(W, X5, torch.empty((5, 64), device=DEV), 0)])
     assert e.value.status == zq.ERR_UNSUPPORTED
+
+
+@pytest.mark.parametrize("xdt", ["f16", "bf16"])
+def test_plan_m4_long_k(xdt):
+    """m = 4 rows of k = 18944 (the 7B down projection's K): the staged
+    activations take most of the LDS; two phases so the counter is reused."""
+    m, k = 4, 18944
+    probs, refs = [], []
+    for i, n in enumerate([640, 384]):
+        q, s, p, W = weight(4, 128, n, k, seed=300 + i)
+        x = synth.normal(synth.rng(400 + i), (m, k), xdt)
+        Y = torch.full((m, n), float("nan"), device=DEV)
+        probs.append((W, x_dev(x, xdt), Y, i))
+        refs.append((q, s, p, x, n))
+    plan = zq.Plan(probs)
+    for _ in range(2):
+        plan.run()
+        torch.cuda.synchronize()
+    plan.check()
+    for (W, X, Y, _), (q, s, p, x, n) in zip(probs, refs):
+        yref = O.gemm(p, 4, s, 128, n, k, x, xdt)
+        xn = np.sqrt((x64(x, xdt) ** 2).sum(1))[:, None]
+        tol = 2e-3 * xn * np.abs(O.dequant(q, 128, s)).max(1)[None, :] + 1e-3 * np.abs(yref)
+        assert np.all(np.abs(Y.double().cpu().numpy() - yref) <= tol)
+        assert torch.equal(zq.gemm(W, X), Y)

@@ -238,8 +238,9 @@ struct zq_plan_s {
   zq::StreamPhase* segs = nullptr;     // device
   zq::StreamProblem* probs = nullptr;  // device
   int2* ranges = nullptr;              // device: [segment][workgroup] {first, last}
-  uint32_t* sync = nullptr;            // device: counter, error word
+  uint32_t* sync = nullptr;            // device: counter, error word, finished workgroups
   int nseg = 0;
+  bool waits = false;  // some segment waits for an earlier phase
   int64_t m = 1;
   int variant = 12;  // one format for all segments, or 12 for a mix
   size_t lds = 0;
@@ -380,17 +381,18 @@ zq_status zq_plan_create(const zq_problem* problems, int count, int64_t m, zq_pl
   plan->m = m;
   plan->lds = lds;
   plan->variant = variant;
+  for (const zq::StreamPhase& sg : fitted) plan->waits = plan->waits || sg.wait;
   hipError_t e = hipMalloc(&plan->segs, sizeof(zq::StreamPhase) * fitted.size());
   if (e == hipSuccess) e = hipMalloc(&plan->probs, sizeof(zq::StreamProblem) * probs.size());
   if (e == hipSuccess) e = hipMalloc(&plan->ranges, sizeof(int2) * ranges.size());
-  if (e == hipSuccess) e = hipMalloc(&plan->sync, 2 * sizeof(uint32_t));
+  if (e == hipSuccess) e = hipMalloc(&plan->sync, 3 * sizeof(uint32_t));
   if (e == hipSuccess)
     e = hipMemcpy(plan->segs, fitted.data(), sizeof(zq::StreamPhase) * fitted.size(), hipMemcpyHostToDevice);
   if (e == hipSuccess)
     e = hipMemcpy(plan->probs, probs.data(), sizeof(zq::StreamProblem) * probs.size(), hipMemcpyHostToDevice);
   if (e == hipSuccess)
     e = hipMemcpy(plan->ranges, ranges.data(), sizeof(int2) * ranges.size(), hipMemcpyHostToDevice);
-  if (e == hipSuccess) e = hipMemset(plan->sync, 0, 2 * sizeof(uint32_t));
+  if (e == hipSuccess) e = hipMemset(plan->sync, 0, 3 * sizeof(uint32_t));
   if (e != hipSuccess) {
     (void)hipFree(plan->segs);
     (void)hipFree(plan->probs);
@@ -406,7 +408,7 @@ zq_status zq_plan_create(const zq_problem* problems, int count, int64_t m, zq_pl
 zq_status zq_plan_run(zq_plan plan, void* stream) {
   if (!plan) return fail(ZQ_ERR_INVALID_ARG, "null plan");
   hipError_t e = zq::launch_stream_plan(plan->segs, plan->nseg, plan->probs, plan->ranges, plan->m,
-                                        plan->variant, plan->lds, plan->sync, (hipStream_t)stream);
+                                        plan->variant, plan->lds, plan->sync, plan->waits, (hipStream_t)stream);
   return e == hipSuccess ? ok() : hip_fail(e, "plan launch");
 }
 

@@ -61,7 +61,7 @@ hipError_t launch_stream_single(const StreamProblem& p, int64_t m, hipStream_t s
 // every segment, or 12 for a mix; sync = 2 device words (counter, error)
 hipError_t launch_stream_plan(const StreamPhase* dev_segs, int nseg, const StreamProblem* dev_probs,
                               const int2* dev_ranges, int64_t m, int variant, size_t lds, uint32_t* sync,
-                              hipStream_t stream);
+                              bool waits, hipStream_t stream);
 
 // vector-ALU kernel for m <= 4 with x staged in LDS
 size_t gemv_valu_lds_bytes(int bits, int64_t m, int64_t k);

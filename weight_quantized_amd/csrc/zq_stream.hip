@@ -4,10 +4,6 @@
 
 namespace zq {
 
-__global__ void reset_sync_kernel(uint32_t* sync) {
-  if (threadIdx.x < 2) sync[threadIdx.x] = 0;
-}
-
 int stream_grid() { return device_info().num_cus; }
 
 int stream_variant_of(int xt, int bits, int group) { return stream_variant(xt, bits, group); }
@@ -63,18 +59,18 @@ hipError_t launch_stream_single(const StreamProblem& p, int64_t m, hipStream_t s
 
 hipError_t launch_stream_plan(const StreamPhase* dev_segs, int nseg, const StreamProblem* dev_probs,
                               const int2* dev_ranges, int64_t m, int variant, size_t lds, uint32_t* sync,
-                              hipStream_t stream) {
+                              bool waits, hipStream_t stream) {
   const void* fn = stream_kernel_for(m, variant);
   hipError_t e = ensure_lds_attr(fn, lds);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(reset_sync_kernel, dim3(1), dim3(64), 0, stream, sync);
-  e = hipGetLastError();
   if (e != hipSuccess) return e;
   StreamPhase dseg{};
   StreamProblem dpr{};
   void* args[] = {(void*)&dev_segs, &nseg, (void*)&dev_probs, (void*)&dev_ranges, &dseg, &dpr, &sync};
-  return hipLaunchCooperativeKernel(fn, dim3(stream_grid()), dim3(m == 1 ? 1024 : 512), args,
-                                    (unsigned)lds, stream);
+  const dim3 grid(stream_grid()), block(m == 1 ? 1024 : 512);
+  // workgroups wait for each other only across phases: only then must they
+  // all be resident at once
+  if (waits) return hipLaunchCooperativeKernel(fn, grid, block, args, (unsigned)lds, stream);
+  return hipLaunchKernel(fn, grid, block, args, lds, stream);
 }
 
 }  // namespace zq

@@ -23,8 +23,8 @@
 // Inside a workgroup's range:
 //   * the products it touches are described by records in LDS; the
 //     activations of each are staged in LDS in decoder order (see Decoder)
-//     with two sums per 16-byte chunk (even and odd k) that remove the
-//     decoder's constant offsets;
+//     with two sums per 128-wide group of k (even and odd k) that remove the
+//     decoder's constant offsets (applied by the group's first lane);
 //   * its 16-lane groups each get an equal, contiguous run of 16-chunk steps
 //     (a step = 256 contiguous bytes of one row), so work is balanced to one
 //     chunk per lane whatever the shapes;
@@ -100,11 +100,18 @@ struct ProdRec {
 };
 static_assert(sizeof(ProdRec) == 64, "LDS record layout");
 
+// Activation block of one 16-chunk step: for each row m, PC rows of 16
+// 16-byte pieces, then the (even, odd) sums of the step's 128-wide groups.
+__host__ __device__ inline size_t stream_block_bytes(int bits, int64_t mr) {
+  const int64_t wpc = 128 / bits, pc = wpc / 8, ng = 16 * wpc / 128;
+  return (size_t)(mr * pc * 256 + mr * ng * 8);
+}
+
 // LDS bytes of one workgroup's view of a segment touching nrec products
 __host__ __device__ inline size_t stream_seg_lds(int bits, int64_t mr, int64_t k, int nrec) {
-  const int64_t wpc = 128 / bits, pc = wpc / 8, C = k / wpc;
+  const int64_t C = k / (128 / bits);
   const int nw = mr == 1 ? 16 : 8;  // waves
-  return (size_t)nrec * 64 + (size_t)nrec * mr * C * (pc + 1) * 16 + (size_t)nw * (8 + 32 * mr);
+  return (size_t)nrec * 64 + (size_t)nrec * (C / 16) * stream_block_bytes(bits, mr) + (size_t)nw * (8 + 32 * mr);
 }
 
 // 16 bytes of activations, optionally with agent-coherent loads (the buffer
@@ -204,9 +211,10 @@ __device__ __forceinline__ void run_segment(const StreamPhase& seg, const Stream
   ProdRec* rec = reinterpret_cast<ProdRec*>(smem);
   // activation slot of one product: blocks of 16 chunks (one step); block b
   // holds, for each row m, PC rows of 16 pieces (piece t of chunk 16b+jj at
-  // (m*(PC+1) + t)*256 + jj*16) and then 16 float4 sums (even, odd, 0, 0), so
-  // a lane reads everything of its chunk at constant offsets from one pointer
-  constexpr int BS = MR * (PC + 1) * 256;  // bytes per block
+  // (m*PC + t)*256 + jj*16), then for each row m the NG (even, odd) sums of
+  // the block's groups at MR*PC*256 + (m*NG + g)*8
+  constexpr int NG = 16 / CPG;                     // groups per block
+  constexpr int BS = MR * PC * 256 + MR * NG * 8;  // bytes per block
   const size_t slot_bytes = (size_t)CB * BS;
   uint8_t* xbase = smem + (size_t)nrec * sizeof(ProdRec);
   int32_t* head_q = reinterpret_cast<int32_t*>(xbase + nrec * slot_bytes);  // [NW] quad of the head
@@ -349,15 +357,20 @@ __device__ __forceinline__ void run_segment(const StreamPhase& seg, const Stream
         piece[1] = v[2] | ((uint32_t)v[3] << 16);
         piece[2] = v[4] | ((uint32_t)v[5] << 16);
         piece[3] = v[6] | ((uint32_t)v[7] << 16);
-        *reinterpret_cast<u4*>(blk + (m * (PC + 1) + t) * 256) = piece;
+        *reinterpret_cast<u4*>(blk + (m * PC + t) * 256) = piece;
       }
+      // the 16 pieces of a 128-group are 16 consecutive, 16-aligned piece
+      // indices (k/8 is a multiple of 16), hence 16 aligned lanes, all live
+      // or all not
 #pragma unroll
-      for (int o = 1; o < PC; o <<= 1) {
+      for (int o = 1; o < 16; o <<= 1) {
         se += __shfl_xor(se, o, 64);
         so += __shfl_xor(so, o, 64);
       }
-      if (live && t == 0)
-        *reinterpret_cast<f4*>(blk + (m * (PC + 1) + PC) * 256) = f4{se, so, 0.f, 0.f};
+      if (live && ((c % CPG) * PC + t) == 0) {
+        uint8_t* sums = xbase + slot * slot_bytes + (size_t)(c / 16) * BS + MR * PC * 256;
+        *reinterpret_cast<f2*>(sums + (m * NG + (c % 16) / CPG) * 8) = f2{se, so};
+      }
     }
   };
 
@@ -401,6 +414,10 @@ __device__ __forceinline__ void run_segment(const StreamPhase& seg, const Stream
   const uint8_t* slot0 = xbase + pi * slot_bytes + j * 16;  // block 0 of this product, lane j
   const uint8_t* xp8 = slot0 + (size_t)cb * BS;            // block of the current step
   bool split_head = cb != 0;  // the run starts inside a quad
+  // the first lane of each group removes the group's decoder offsets
+  const int sdelta = MR * PC * 256 + (j / CPG) * 8 - j * 16;  // sums of lane j's group, from xp8
+  const bool gfirst = j % CPG == 0;
+  const float fe = gfirst ? FD::BE : 0.f, fo = gfirst ? FD::BO : 0.f;
   float acc[MR];
 #pragma unroll
   for (int m = 0; m < MR; ++m) acc[m] = 0.f;
@@ -425,7 +442,7 @@ __device__ __forceinline__ void run_segment(const StreamPhase& seg, const Stream
 #pragma unroll
             for (int t = (dw * CD::PAIRS) / 4; t < ((dw + 1) * CD::PAIRS + 3) / 4; ++t) {
               if ((dw * CD::PAIRS) % 4 == 0 || t > (dw * CD::PAIRS) / 4) {
-                const u4 pc = *reinterpret_cast<const u4*>(xp8 + (m * (PC + 1) + t) * 256);
+                const u4 pc = *reinterpret_cast<const u4*>(xp8 + (m * PC + t) * 256);
                 xp[4 * t + 0] = pc[0];
                 xp[4 * t + 1] = pc[1];
                 xp[4 * t + 2] = pc[2];
@@ -434,8 +451,8 @@ __device__ __forceinline__ void run_segment(const StreamPhase& seg, const Stream
             }
             d = FD::dot(wq[dw], xp + dw * CD::PAIRS, d);
           }
-          const f4 xsm = *reinterpret_cast<const f4*>(xp8 + (m * (PC + 1) + PC) * 256);
-          const float part = d - FD::BE * xsm[0] - FD::BO * xsm[1];
+          const f2 xsm = *reinterpret_cast<const f2*>(xp8 + sdelta + m * NG * 8);
+          const float part = d - fe * xsm[0] - fo * xsm[1];
           if constexpr (GROUPED) acc[m] = __builtin_fmaf(sc, part, acc[m]);
           else acc[m] += part;
         }
@@ -552,7 +569,8 @@ __device__ __forceinline__ void seg_dispatch(const StreamPhase& seg, const Strea
 // Single product: segs == nullptr, `single_seg` and `single_prob` by value.
 // Plan: nseg segments, the problem table, per-(segment, workgroup) problem
 // ranges wranges[s * G + w] = {first, last} (within the segment), and
-// sync = {done counter, error word}. VAR fixes the format (VAR_ANY: a mix).
+// sync = {done counter, error word, finished workgroups}; the counters are
+// zero when a run starts and the run leaves them zero. VAR fixes the format (VAR_ANY: a mix).
 template <int MR, int VAR>
 __global__ __launch_bounds__(st_threads<MR>()) void gemv_stream_kernel(
     const StreamPhase* __restrict__ segs, int nseg, const StreamProblem* __restrict__ probs,
@@ -578,6 +596,16 @@ __global__ __launch_bounds__(st_threads<MR>()) void gemv_stream_kernel(
     }
     const int2 wr = wranges[(int64_t)s * G + blockIdx.x];
     seg_dispatch<MR, VAR>(seg, probs, single_prob, wr, smem, ws, waits * G, true);
+  }
+  if (waits) {
+    // leave the counter at zero for the next run: the last workgroup to get
+    // here knows that no workgroup polls it any more
+    __syncthreads();
+    if (threadIdx.x == 0 &&
+        __hip_atomic_fetch_add(sync + 2, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == G - 1) {
+      __hip_atomic_store(sync + 0, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(sync + 2, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
