@@ -183,18 +183,23 @@ zq_status zq_gemm(const zq_weight* W, const void* X, zq_dtype x_dtype, int64_t m
  *              (q,k,v -> o -> gate,up -> down of a decoder layer). Problems of
  *              one phase are independent and must not write what another one
  *              of that phase reads. Consecutive problems of a phase that share
- *              k, bits, group and x dtype (up to 4) are streamed as one row
- *              space; problems that share an activation buffer stage it once.
+ *              k, bits, group and x dtype are streamed as one row space (any
+ *              number of them), split evenly over the workgroups.
  * zq_plan_create  validates every problem (as zq_gemm does), requires
- *              1 <= m <= 4, packed rows whose byte length is a multiple of 256
- *              and 16-byte aligned pointers (ZQ_ERR_UNSUPPORTED otherwise),
- *              copies the list to device memory and allocates two device words
- *              for the phase counter. Pointers inside the problems are used at
- *              every run: the caller keeps those buffers alive.
- * zq_plan_run  enqueues the plan on `stream` (two launches: a counter reset
- *              and one cooperative kernel with one workgroup per CU);
- *              allocates nothing. Runs of one plan on different streams at
- *              the same time race on its counter.
+ *              1 <= m <= 4, packed rows whose byte length is a multiple of 256,
+ *              16-byte aligned pointers and activations of one problem that
+ *              fit in the 160 KiB of LDS with their group sums (m * k * 2
+ *              bytes plus 1/32 of that; INT4 at m = 4 takes k up to 19456)
+ *              (ZQ_ERR_UNSUPPORTED otherwise),
+ *              copies the list to device memory and allocates three device
+ *              words (phase counter, error word, finished workgroups).
+ *              Pointers inside the problems are used at every run: the caller
+ *              keeps those buffers alive.
+ * zq_plan_run  enqueues the plan on `stream`: one launch with one workgroup
+ *              per CU (cooperative when the plan has more than one phase, so
+ *              all workgroups are resident); allocates nothing; the run leaves
+ *              the counter at zero for the next one. Runs of one plan that
+ *              overlap (on different streams) race on its counter.
  * zq_plan_check synchronises the device and reports ZQ_ERR_HIP if a phase
  *              wait in an earlier run gave up (its outputs are then invalid).
  * zq_plan_destroy frees the plan's device memory (synchronises the device).
