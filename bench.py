@@ -68,7 +68,7 @@ def parse():
                             "hbm-copy"])
     p.add_argument("--m", type=int, default=None, help="activation rows (qwen7b-batch)")
     p.add_argument("--launch", default=None, choices=["plan", "graph", "eager"],
-                   help="plan: one resident launch per step (m <= 4, the default there); "
+                   help="plan: one resident launch per step (m <= 32, the default there); "
                         "graph: the per-projection launches replayed as a HIP graph")
     p.add_argument("--order", default="independent", choices=["chained", "independent"],
                    help="plan phases: independent = every product of the step at once (each has its "
@@ -263,7 +263,7 @@ def main():
     stack = Stack(a.config, a.m, a.layers, torch, zq, synth)
 
     if a.launch is None:
-        a.launch = "plan" if stack.m <= 4 else "graph"
+        a.launch = "plan" if stack.m <= 32 else "graph"
     # ---- timed region
     graph = None
     if a.launch == "plan":

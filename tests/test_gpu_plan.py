@@ -134,9 +134,9 @@ def test_plan_validation():
     with pytest.raises(zq.ZqError) as e:
         zq.Plan([(W, X, torch.empty((1, 64), device=DEV), 1), (W, X, torch.empty((1, 64), device=DEV), 0)])
     assert e.value.status == zq.ERR_INVALID_ARG
-    X5 = torch.zeros((5, 512), dtype=torch.float16, device=DEV)
+    X33 = torch.zeros((33, 512), dtype=torch.float16, device=DEV)
     with pytest.raises(zq.ZqError) as e:
-        zq.Plan([(W, X5, torch.empty((5, 64), device=DEV), 0)])
+        zq.Plan([(W, X33, torch.empty((33, 64), device=DEV), 0)])
     assert e.value.status == zq.ERR_UNSUPPORTED
 
 

@@ -207,7 +207,10 @@ zq_status zq_gemm(const zq_weight* W, const void* X, zq_dtype x_dtype, int64_t m
   const int64_t rowbytes = W->k * W->bits / 8;
   const bool aligned16 = ((uintptr_t)W->packed & 15) == 0 && rowbytes % 16 == 0 &&
                          ((uintptr_t)X & 15) == 0 && (m == 1 || (ldx * 2) % 16 == 0);
-  if (m <= 4 && aligned16 && zq::stream_supported(W->bits, W->group, m, W->n, W->k)) {
+  const bool use_stream = m <= 4 && aligned16 && zq::stream_supported(W->bits, W->group, m, W->n, W->k);
+  const bool use_mstream = !use_stream && m >= zq::MSTREAM_MIN_M &&
+                           zq::mstream_supported(W->packed, W->scales, W->bits, W->group, m, W->k, X, ldx);
+  if (use_stream || use_mstream) {
     zq::StreamProblem p{};
     p.packed = a.packed;
     p.scales = a.scales;
@@ -222,7 +225,7 @@ zq_status zq_gemm(const zq_weight* W, const void* X, zq_dtype x_dtype, int64_t m
     p.xt = a.xt;
     p.yt = a.yt;
     p.row_off = 0;
-    e = zq::launch_stream_single(p, m, s);
+    e = use_stream ? zq::launch_stream_single(p, m, s) : zq::launch_mstream_single(p, m, s);
   } else if (m <= 4 && aligned16 && zq::gemv_valu_lds_bytes(W->bits, m, W->k) <= 64 * 1024)
     e = zq::launch_gemv_valu(a);
   else if (aligned16 && zq::gemm_mfma_supported(a))
@@ -241,6 +244,7 @@ struct zq_plan_s {
   uint32_t* sync = nullptr;            // device: counter, error word, finished workgroups
   int nseg = 0;
   bool waits = false;  // some segment waits for an earlier phase
+  bool mfma = false;   // the MFMA batched-decode kernel (m >= MSTREAM_MIN_M)
   int64_t m = 1;
   int variant = 12;  // one format for all segments, or 12 for a mix
   size_t lds = 0;
@@ -272,7 +276,8 @@ zq_status zq_plan_create(const zq_problem* problems, int count, int64_t m, zq_pl
   if (!plan_out) return fail(ZQ_ERR_INVALID_ARG, "null plan_out");
   *plan_out = nullptr;
   if (count < 1 || !problems) return fail(ZQ_ERR_INVALID_ARG, "empty problem list");
-  if (m < 1 || m > 4) return fail(ZQ_ERR_UNSUPPORTED, "plans take 1 <= m <= 4 (m=%lld)", (long long)m);
+  if (m < 1 || m > 32) return fail(ZQ_ERR_UNSUPPORTED, "plans take 1 <= m <= 32 (m=%lld)", (long long)m);
+  const bool mfma = m >= zq::MSTREAM_MIN_M;
   std::vector<zq::StreamProblem> probs(count);
   std::vector<zq::StreamPhase> segs;
   for (int i = 0; i < count; ++i) {
@@ -290,9 +295,14 @@ zq_status zq_plan_create(const zq_problem* problems, int count, int64_t m, zq_pl
       return fail(ZQ_ERR_UNSUPPORTED, "problem %d: empty shapes and null pointers are not planned", i);
     const bool aligned = ((uintptr_t)q.w.packed & 15) == 0 && ((uintptr_t)q.x & 15) == 0 &&
                          (m == 1 || (q.ldx * 2) % 16 == 0);
-    if (!aligned || !zq::stream_supported(q.w.bits, q.w.group, m, q.w.n, q.w.k))
+    if (mfma) {
+      if (!zq::mstream_supported(q.w.packed, q.w.scales, q.w.bits, q.w.group, m, q.w.k, q.x, q.ldx))
+        return fail(ZQ_ERR_UNSUPPORTED, "problem %d: plans with m >= %d need INT4 codes, k a multiple of 512, "
+                    "16-byte aligned codes and activations and 8-byte aligned scales", i, zq::MSTREAM_MIN_M);
+    } else if (!aligned || !zq::stream_supported(q.w.bits, q.w.group, m, q.w.n, q.w.k)) {
       return fail(ZQ_ERR_UNSUPPORTED, "problem %d: needs 16-byte alignment, rows of 256-byte multiples "
                   "and activations that fit in LDS", i);
+    }
     const int xt = q.x_dtype == ZQ_F16 ? zq::XF16 : zq::XBF16;
     // a new segment when the phase or the format changes
     const bool same_phase = i > 0 && q.phase == problems[i - 1].phase;
@@ -352,7 +362,7 @@ zq_status zq_plan_create(const zq_problem* problems, int count, int64_t m, zq_pl
       seg_ranges(sg, probs, G, r);
       int maxrec = 1;
       for (const int2& v : r) maxrec = std::max(maxrec, v.y - v.x + 1);
-      const size_t need = zq::stream_lds_bytes(sg.bits, m, sg.k, maxrec);
+      const size_t need = mfma ? zq::mstream_lds(m, maxrec) : zq::stream_lds_bytes(sg.bits, m, sg.k, maxrec);
       if (need > zq::STREAM_LDS_MAX) {
         if (sg.count == 1)
           return fail(ZQ_ERR_UNSUPPORTED, "problem %d needs %zu bytes of LDS (max %zu)", sg.first, need,
@@ -373,8 +383,8 @@ zq_status zq_plan_create(const zq_problem* problems, int count, int64_t m, zq_pl
   }
   int variant = -1;
   for (const zq::StreamPhase& sg : fitted) {
-    const int v = zq::stream_variant_of(sg.xt, sg.bits, sg.group);
-    variant = (variant == -1 || variant == v) ? v : 12;
+    const int v = mfma ? zq::mstream_variant_of(sg.xt, sg.group) : zq::stream_variant_of(sg.xt, sg.bits, sg.group);
+    variant = (variant == -1 || variant == v) ? v : (mfma ? 4 : 12);
   }
   zq_plan_s* plan = new zq_plan_s;
   plan->nseg = (int)fitted.size();
@@ -382,6 +392,7 @@ zq_status zq_plan_create(const zq_problem* problems, int count, int64_t m, zq_pl
   plan->lds = lds;
   plan->variant = variant;
   for (const zq::StreamPhase& sg : fitted) plan->waits = plan->waits || sg.wait;
+  plan->mfma = mfma;
   hipError_t e = hipMalloc(&plan->segs, sizeof(zq::StreamPhase) * fitted.size());
   if (e == hipSuccess) e = hipMalloc(&plan->probs, sizeof(zq::StreamProblem) * probs.size());
   if (e == hipSuccess) e = hipMalloc(&plan->ranges, sizeof(int2) * ranges.size());
@@ -407,8 +418,11 @@ zq_status zq_plan_create(const zq_problem* problems, int count, int64_t m, zq_pl
 
 zq_status zq_plan_run(zq_plan plan, void* stream) {
   if (!plan) return fail(ZQ_ERR_INVALID_ARG, "null plan");
-  hipError_t e = zq::launch_stream_plan(plan->segs, plan->nseg, plan->probs, plan->ranges, plan->m,
-                                        plan->variant, plan->lds, plan->sync, plan->waits, (hipStream_t)stream);
+  hipError_t e = plan->mfma
+                     ? zq::launch_mstream_plan(plan->segs, plan->nseg, plan->probs, plan->ranges, plan->m,
+                                               plan->variant, plan->lds, plan->sync, plan->waits, (hipStream_t)stream)
+                     : zq::launch_stream_plan(plan->segs, plan->nseg, plan->probs, plan->ranges, plan->m,
+                                              plan->variant, plan->lds, plan->sync, plan->waits, (hipStream_t)stream);
   return e == hipSuccess ? ok() : hip_fail(e, "plan launch");
 }
 

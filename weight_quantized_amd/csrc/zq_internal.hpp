@@ -63,6 +63,19 @@ hipError_t launch_stream_plan(const StreamPhase* dev_segs, int nseg, const Strea
                               const int2* dev_ranges, int64_t m, int variant, size_t lds, uint32_t* sync,
                               bool waits, hipStream_t stream);
 
+// persistent MFMA kernel for batched decode: INT4, 2 <= m <= 32, k a
+// multiple of 512, 16-byte aligned codes and activations, 8-byte aligned
+// group scales
+constexpr int MSTREAM_MIN_M = 5;
+bool mstream_supported(const void* packed, const uint16_t* scales, int bits, int group, int64_t m, int64_t k,
+                       const void* x, int64_t ldx);
+size_t mstream_lds(int64_t m, int nrec);
+int mstream_variant_of(int xt, int group);  // 4 = a mix
+hipError_t launch_mstream_single(const StreamProblem& p, int64_t m, hipStream_t stream);
+hipError_t launch_mstream_plan(const StreamPhase* dev_segs, int nseg, const StreamProblem* dev_probs,
+                               const int2* dev_ranges, int64_t m, int variant, size_t lds, uint32_t* sync,
+                               bool waits, hipStream_t stream);
+
 // vector-ALU kernel for m <= 4 with x staged in LDS
 size_t gemv_valu_lds_bytes(int bits, int64_t m, int64_t k);
 hipError_t launch_gemv_valu(const GemmArgs& a);

@@ -1,0 +1,8 @@
+// zq_mstream_t2.hip -- instantiations of the persistent MFMA batched-decode
+// kernel with 2 tile(s) of 16 activation rows (one translation unit each
+// keeps builds parallel).
+#include "zq_mstream_impl.hpp"
+
+namespace zq {
+const void* mstream_kernel_t2(int var) { return mstream_fn_var<2>(var); }
+}  // namespace zq

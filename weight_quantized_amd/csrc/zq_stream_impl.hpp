@@ -581,6 +581,10 @@ __global__ __launch_bounds__(st_threads<MR>()) void gemv_stream_kernel(
     seg_dispatch<MR, VAR>(single_seg, nullptr, single_prob, make_int2(0, 0), smem, nullptr, 0, false);
     return;
   }
+  // data crosses phases only when some segment waits: only then do the
+  // activations and outputs need agent-coherent (L2-bypassing) accesses
+  bool coh = false;
+  for (int s = 0; s < nseg; ++s) coh = coh || segs[s].wait;
   uint32_t waits = 0;
   for (int s = 0; s < nseg; ++s) {
     const StreamPhase seg = segs[s];
@@ -595,7 +599,7 @@ __global__ __launch_bounds__(st_threads<MR>()) void gemv_stream_kernel(
       ws = sync;
     }
     const int2 wr = wranges[(int64_t)s * G + blockIdx.x];
-    seg_dispatch<MR, VAR>(seg, probs, single_prob, wr, smem, ws, waits * G, true);
+    seg_dispatch<MR, VAR>(seg, probs, single_prob, wr, smem, ws, waits * G, coh);
   }
   if (waits) {
     // leave the counter at zero for the next run: the last workgroup to get
