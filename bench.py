@@ -74,6 +74,10 @@ def parse():
                    help="plan phases: independent = every product of the step at once (each has its "
                         "own activations); chained = q,k,v -> o -> gate,up -> down per layer, each "
                         "phase waiting for the previous one, as a decoder's data flow would")
+    p.add_argument("--streams", type=int, default=None,
+                   help="graph launch: spread the step's independent products over this many streams "
+                        "inside the captured graph, so small kernels run side by side (default 4 for "
+                        "prefill, 1 otherwise)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--layers", type=int, default=None, help="override the layer count (profiling)")
     return p.parse_args()
@@ -149,13 +153,34 @@ class Stack:
     def plan_step(self):
         self.plan.run()
 
-    def step(self):
-        s = self.torch.cuda.current_stream().cuda_stream
+    def step(self, streams=None):
+        """every product of the step; with `streams`, product i goes to stream
+        i % len(streams) (forked from and joined back to the current stream)"""
+        torch = self.torch
         fn = self._fn
-        for a in self._args:
-            st = fn(*a, s)
+        if not streams:
+            s = torch.cuda.current_stream().cuda_stream
+            for a in self._args:
+                st = fn(*a, s)
+                if st:
+                    raise RuntimeError(f"zq_gemm failed: {self.zq.lib().zq_last_error().decode()}")
+            return
+        cur = torch.cuda.current_stream()
+        fork = torch.cuda.Event()
+        fork.record(cur)
+        for sm in streams:
+            sm.wait_event(fork)
+        # largest products first, dealt round-robin
+        order = sorted(range(len(self._args)), key=lambda i: -self.launches[i][0].n * self.launches[i][0].k)
+        for pos, i in enumerate(order):
+            sm = streams[pos % len(streams)]
+            st = fn(*self._args[i], sm.cuda_stream)
             if st:
                 raise RuntimeError(f"zq_gemm failed: {self.zq.lib().zq_last_error().decode()}")
+        for sm in streams:
+            join = torch.cuda.Event()
+            join.record(sm)
+            cur.wait_event(join)
 
     def step_timed_launches(self, ev):
         """eager step with an event pair around every launch"""
@@ -270,15 +295,18 @@ def main():
         stack.make_plan(a.order)
         run = stack.plan_step
     elif a.launch == "graph":
+        if a.streams is None:
+            a.streams = 4 if a.config == "qwen7b-prefill" else 1
+        streams = [torch.cuda.Stream() for _ in range(a.streams)] if a.streams > 1 else None
         side = torch.cuda.Stream()
         side.wait_stream(torch.cuda.current_stream())
         with torch.cuda.stream(side):
-            stack.step()
+            stack.step(streams)
         torch.cuda.current_stream().wait_stream(side)
         torch.cuda.synchronize()
         graph = torch.cuda.CUDAGraph()
         with torch.cuda.graph(graph):
-            stack.step()
+            stack.step(streams)
         run = graph.replay
     else:
         run = stack.step
@@ -358,6 +386,7 @@ def main():
         "weight_bytes_per_step": stack.weight_bytes, "launch": a.launch, "order": a.order if a.launch == "plan" else "stream",
         "launches_per_step": 1 if a.launch == "plan" else len(stack.launches),
         "wall_ms_per_step": round(wall_ms, 5), "avg_kernel_us": round(avg_launch_ms * 1e3, 3),
+        "streams": a.streams if a.launch == "graph" else 1,
         "settle_s": SETTLE_S}
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(stack, torch, synth)

@@ -228,6 +228,8 @@ zq_status zq_gemm(const zq_weight* W, const void* X, zq_dtype x_dtype, int64_t m
     e = use_stream ? zq::launch_stream_single(p, m, s) : zq::launch_mstream_single(p, m, s);
   } else if (m <= 4 && aligned16 && zq::gemv_valu_lds_bytes(W->bits, m, W->k) <= 64 * 1024)
     e = zq::launch_gemv_valu(a);
+  else if (aligned16 && zq::gemm_prefill2_supported(a))
+    e = zq::launch_gemm_prefill2(a);
   else if (aligned16 && zq::gemm_mfma_supported(a))
     e = zq::launch_gemm_mfma(a);
   else

@@ -79,6 +79,9 @@ hipError_t launch_mstream_plan(const StreamPhase* dev_segs, int nseg, const Stre
 // vector-ALU kernel for m <= 4 with x staged in LDS
 size_t gemv_valu_lds_bytes(int bits, int64_t m, int64_t k);
 hipError_t launch_gemv_valu(const GemmArgs& a);
+// prefill MFMA kernel: m > 64, one scale per tensor, k a multiple of 64
+bool gemm_prefill2_supported(const GemmArgs& a);
+hipError_t launch_gemm_prefill2(const GemmArgs& a);
 // MFMA kernels for larger m
 bool gemm_mfma_supported(const GemmArgs& a);
 hipError_t launch_gemm_mfma(const GemmArgs& a);
