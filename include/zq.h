@@ -161,8 +161,18 @@ zq_status zq_gemv(const zq_weight* W, const void* x, zq_dtype x_dtype, void* y,
  *           dtype ZQ_F16 or ZQ_BF16.
  *   Y       device, m rows of n elements, row stride ldy >= n, dtype ZQ_F32,
  *           ZQ_F16 or ZQ_BF16.
- * Small m runs on a vector-ALU kernel; larger m dequantizes weight tiles to
- * bf16 / fp16 (exact for every code) and runs the contraction on MFMA.
+ * Kernels by shape (all give results within the same tolerance of the exact
+ * sums; integer-valued inputs give exact sums on every path):
+ *   m = 1 (and m <= 4 for INT2/INT8): a vector-ALU kernel that streams the
+ *     codes once with 128-bit loads;
+ *   m = 2..32, INT4, k a multiple of 512, 16-byte aligned codes and
+ *     activations, 8-byte aligned scales: a resident MFMA kernel that streams
+ *     the codes once;
+ *   m > 64, one scale per tensor, k a multiple of 64: a tiled MFMA kernel
+ *     (256 x 256 tiles) that decodes codes in registers;
+ *   anything else: tiled MFMA kernels, or a general kernel for unaligned and
+ *     odd shapes.
+ * Codes are decoded to bf16 / fp16 values that are exact for every code.
  * Asynchronous on `stream`.
  */
 zq_status zq_gemm(const zq_weight* W, const void* X, zq_dtype x_dtype, int64_t m,
@@ -185,12 +195,15 @@ zq_status zq_gemm(const zq_weight* W, const void* X, zq_dtype x_dtype, int64_t m
  *              of that phase reads. Consecutive problems of a phase that share
  *              k, bits, group and x dtype are streamed as one row space (any
  *              number of them), split evenly over the workgroups.
- * zq_plan_create  validates every problem (as zq_gemm does), requires
- *              1 <= m <= 4, packed rows whose byte length is a multiple of 256,
- *              16-byte aligned pointers and activations of one problem that
- *              fit in the 160 KiB of LDS with their group sums (m * k * 2
- *              bytes plus 1/32 of that; INT4 at m = 4 takes k up to 19456)
- *              (ZQ_ERR_UNSUPPORTED otherwise),
+ * zq_plan_create  validates every problem (as zq_gemm does) and requires
+ *              1 <= m <= 32 (ZQ_ERR_UNSUPPORTED otherwise). For m >= 2, when
+ *              every problem is INT4 with k a multiple of 512, 16-byte aligned
+ *              codes and activations and 8-byte aligned scales, the plan runs
+ *              on the MFMA kernel; otherwise (m <= 4 only) on the vector-ALU
+ *              kernel, which needs packed rows whose byte length is a multiple
+ *              of 256, 16-byte aligned pointers and activations of one problem
+ *              that fit in the 160 KiB of LDS with their group sums (m * k * 2
+ *              bytes plus 1/32 of that). The plan
  *              copies the list to device memory and allocates three device
  *              words (phase counter, error word, finished workgroups).
  *              Pointers inside the problems are used at every run: the caller

@@ -72,7 +72,12 @@ def test_plan_matches_oracle_and_single_calls(m):
     for (W, X, Y, _), (q, s, p, x, xdt, group, bits, n, k) in zip(probs, refs):
         single = zq.gemm(W, X)
         torch.cuda.synchronize()
-        assert torch.equal(single, Y)                        # same kernel, same split
+        # this plan mixes code widths, so it runs on the vector-ALU kernel;
+        # a single call takes that kernel too for m = 1 and for INT2/INT8,
+        # while single INT4 calls with m >= 2 run on the MFMA kernel (its own
+        # summation order, checked against the oracle below)
+        if m == 1 or bits != 4:
+            assert torch.equal(single, Y)                    # same kernel, same split
         yref = O.gemm(p, bits, s, group, n, k, x, xdt)
         xn = np.sqrt((x64(x, xdt) ** 2).sum(1))[:, None]
         tol = 2e-3 * xn * np.abs(O.dequant(q, group, s)).max(1)[None, :] + 1e-3 * np.abs(yref)

@@ -207,9 +207,10 @@ zq_status zq_gemm(const zq_weight* W, const void* X, zq_dtype x_dtype, int64_t m
   const int64_t rowbytes = W->k * W->bits / 8;
   const bool aligned16 = ((uintptr_t)W->packed & 15) == 0 && rowbytes % 16 == 0 &&
                          ((uintptr_t)X & 15) == 0 && (m == 1 || (ldx * 2) % 16 == 0);
-  const bool use_stream = m <= 4 && aligned16 && zq::stream_supported(W->bits, W->group, m, W->n, W->k);
-  const bool use_mstream = !use_stream && m >= zq::MSTREAM_MIN_M &&
+  const bool use_mstream = m >= zq::MSTREAM_MIN_M &&
                            zq::mstream_supported(W->packed, W->scales, W->bits, W->group, m, W->k, X, ldx);
+  const bool use_stream = !use_mstream && m <= 4 && aligned16 &&
+                          zq::stream_supported(W->bits, W->group, m, W->n, W->k);
   if (use_stream || use_mstream) {
     zq::StreamProblem p{};
     p.packed = a.packed;
@@ -279,7 +280,15 @@ zq_status zq_plan_create(const zq_problem* problems, int count, int64_t m, zq_pl
   *plan_out = nullptr;
   if (count < 1 || !problems) return fail(ZQ_ERR_INVALID_ARG, "empty problem list");
   if (m < 1 || m > 32) return fail(ZQ_ERR_UNSUPPORTED, "plans take 1 <= m <= 32 (m=%lld)", (long long)m);
-  const bool mfma = m >= zq::MSTREAM_MIN_M;
+  // the MFMA kernel when every product suits it; for m <= 4 the vector-ALU
+  // kernel takes the other formats
+  bool mfma = m >= zq::MSTREAM_MIN_M;
+  if (mfma && m <= 4) {
+    for (int i = 0; i < count && mfma; ++i) {
+      const zq_problem& q = problems[i];
+      mfma = zq::mstream_supported(q.w.packed, q.w.scales, q.w.bits, q.w.group, m, q.w.k, q.x, q.ldx);
+    }
+  }
   std::vector<zq::StreamProblem> probs(count);
   std::vector<zq::StreamPhase> segs;
   for (int i = 0; i < count; ++i) {
@@ -299,8 +308,8 @@ zq_status zq_plan_create(const zq_problem* problems, int count, int64_t m, zq_pl
                          (m == 1 || (q.ldx * 2) % 16 == 0);
     if (mfma) {
       if (!zq::mstream_supported(q.w.packed, q.w.scales, q.w.bits, q.w.group, m, q.w.k, q.x, q.ldx))
-        return fail(ZQ_ERR_UNSUPPORTED, "problem %d: plans with m >= %d need INT4 codes, k a multiple of 512, "
-                    "16-byte aligned codes and activations and 8-byte aligned scales", i, zq::MSTREAM_MIN_M);
+        return fail(ZQ_ERR_UNSUPPORTED, "problem %d: plans with m > 4 need INT4 codes, k a multiple of 512, "
+                    "16-byte aligned codes and activations and 8-byte aligned scales", i);
     } else if (!aligned || !zq::stream_supported(q.w.bits, q.w.group, m, q.w.n, q.w.k)) {
       return fail(ZQ_ERR_UNSUPPORTED, "problem %d: needs 16-byte alignment, rows of 256-byte multiples "
                   "and activations that fit in LDS", i);

@@ -66,7 +66,7 @@ hipError_t launch_stream_plan(const StreamPhase* dev_segs, int nseg, const Strea
 // persistent MFMA kernel for batched decode: INT4, 2 <= m <= 32, k a
 // multiple of 512, 16-byte aligned codes and activations, 8-byte aligned
 // group scales
-constexpr int MSTREAM_MIN_M = 5;
+constexpr int MSTREAM_MIN_M = 2;  // measured faster than the VALU kernel from 2 rows on
 bool mstream_supported(const void* packed, const uint16_t* scales, int bits, int group, int64_t m, int64_t k,
                        const void* x, int64_t ldx);
 size_t mstream_lds(int64_t m, int nrec);
