@@ -60,6 +60,16 @@ def lib():
         L.zqo_gemm.argtypes = [vp, i32, vp, i32, i64, i64, vp, i32, i64, i64, vp, i64]
         for f in ("zqo_compute_scales", "zqo_quantize", "zqo_pack", "zqo_gemm"):
             getattr(L, f).restype = ctypes.c_int
+        L.zqo_compute_scales_zeros.argtypes = [vp, i32, i64, i64, i32, vp, vp]
+        L.zqo_quantize_asym.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp]
+        L.zqo_pack_u.argtypes = [vp, i64, i64, i32, vp]
+        L.zqo_unpack_u.argtypes = [vp, i64, i64, i32, vp]
+        L.zqo_unpack_u.restype = None
+        L.zqo_dequant_asym.argtypes = [vp, i64, i64, vp, vp, vp]
+        L.zqo_dequant_asym.restype = None
+        L.zqo_gemm_asym.argtypes = [vp, i32, vp, vp, i64, i64, vp, i32, i64, i64, vp, i64]
+        for f in ("zqo_compute_scales_zeros", "zqo_quantize_asym", "zqo_pack_u", "zqo_gemm_asym"):
+            getattr(L, f).restype = ctypes.c_int
         _lib = L
     return _lib
 
@@ -186,3 +196,77 @@ def gemm_rows(packed: np.ndarray, bits: int, scales: np.ndarray, group: int, n: 
         sc = scales if group == 0 else scales.reshape(n, -1)[r]
         out[:, j] = gemm(packed[r:r + 1], bits, sc, group, 1, k, x2, x_dtype)[:, 0]
     return out
+
+
+# ---------------------------------------------------------------------------
+# asymmetric variant: unsigned codes, fp16 scale and zero point per 128-group
+
+
+def compute_scales_zeros(w: np.ndarray, dtype: str, bits: int):
+    w = _typed(w, dtype)
+    n, k = w.shape
+    sc = np.zeros(n * (k // 128), dtype=np.uint16)
+    zr = np.zeros(n * (k // 128), dtype=np.uint16)
+    st = lib().zqo_compute_scales_zeros(_ptr(w), DTYPES[dtype], n, k, bits, _ptr(sc), _ptr(zr))
+    if st:
+        raise OracleError(st, "compute_scales_zeros")
+    return sc, zr
+
+
+def quantize_asym(w: np.ndarray, dtype: str, bits: int, scales: np.ndarray, zeros: np.ndarray) -> np.ndarray:
+    w = _typed(w, dtype)
+    n, k = w.shape
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    zeros = np.ascontiguousarray(zeros, dtype=np.uint16)
+    codes = np.zeros((n, k), dtype=np.uint8)
+    st = lib().zqo_quantize_asym(_ptr(w), DTYPES[dtype], n, k, bits, _ptr(scales), _ptr(zeros), _ptr(codes))
+    if st:
+        raise OracleError(st, "quantize_asym")
+    return codes
+
+
+def pack_u(codes: np.ndarray, bits: int) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    n, k = codes.shape
+    out = np.zeros((n, k * bits // 8), dtype=np.uint8)
+    st = lib().zqo_pack_u(_ptr(codes), n, k, bits, _ptr(out))
+    if st:
+        raise OracleError(st, "pack_u")
+    return out
+
+
+def unpack_u(packed: np.ndarray, n: int, k: int, bits: int) -> np.ndarray:
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    assert packed.size == n * k * bits // 8
+    out = np.zeros((n, k), dtype=np.uint8)
+    lib().zqo_unpack_u(_ptr(packed), n, k, bits, _ptr(out))
+    return out
+
+
+def dequant_asym(codes: np.ndarray, scales: np.ndarray, zeros: np.ndarray) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint8)
+    n, k = codes.shape
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    zeros = np.ascontiguousarray(zeros, dtype=np.uint16)
+    out = np.zeros((n, k), dtype=np.float64)
+    lib().zqo_dequant_asym(_ptr(codes), n, k, _ptr(scales), _ptr(zeros), _ptr(out))
+    return out
+
+
+def gemm_asym(packed: np.ndarray, bits: int, scales: np.ndarray, zeros: np.ndarray, n: int, k: int,
+              x: np.ndarray, x_dtype: str) -> np.ndarray:
+    """y[m][n] in float64 for x of shape [m][k] (or [k] for one row)."""
+    packed = np.ascontiguousarray(packed, dtype=np.uint8)
+    scales = np.ascontiguousarray(scales, dtype=np.uint16)
+    zeros = np.ascontiguousarray(zeros, dtype=np.uint16)
+    x = _typed(x, x_dtype)
+    one = x.ndim == 1
+    x2 = x.reshape(1, -1) if one else x
+    m = x2.shape[0]
+    assert x2.shape[1] == k
+    y = np.zeros((m, n), dtype=np.float64)
+    st = lib().zqo_gemm_asym(_ptr(packed), bits, _ptr(scales), _ptr(zeros), n, k, _ptr(x2),
+                             DTYPES[x_dtype], m, k, _ptr(y), n)
+    if st:
+        raise OracleError(st, "gemm_asym")
+    return y[0] if one else y

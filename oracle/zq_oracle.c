@@ -230,3 +230,132 @@ int zqo_gemm(const uint8_t* packed, int bits, const uint16_t* scales, int group,
   }
   return ZQO_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Asymmetric variant (ZSE wiki, section on the .zse model format). */
+
+static int asym_shape_ok(int64_t n, int64_t k, int bits) {
+  if (bits != 2 && bits != 4) return ZQO_ERR_UNSUPPORTED;
+  if (n < 0 || k < 0) return ZQO_ERR_INVALID_ARG;
+  if (k % 128 != 0) return ZQO_ERR_UNSUPPORTED;
+  return ZQO_OK;
+}
+
+int zqo_compute_scales_zeros(const void* w, int w_dtype, int64_t n, int64_t k, int bits,
+                             uint16_t* scales, uint16_t* zeros) {
+  int st = asym_shape_ok(n, k, bits);
+  if (st) return st;
+  if (w_dtype != ZQO_F16 && w_dtype != ZQO_BF16 && w_dtype != ZQO_F32)
+    return ZQO_ERR_INVALID_ARG;
+  const double qmax = (double)((1 << bits) - 1);
+  const int64_t gpr = k / 128;
+  for (int64_t r = 0; r < n; ++r) {
+    for (int64_t g = 0; g < gpr; ++g) {
+      double lo = INFINITY, hi = -INFINITY;
+      for (int64_t j = 0; j < 128; ++j) {
+        double v = zqo_widen(w, w_dtype, r * k + g * 128 + j);
+        if (!isfinite(v)) return ZQO_ERR_RANGE;
+        if (v < lo) lo = v;
+        if (v > hi) hi = v;
+      }
+      uint16_t s16 = zqo_f64_to_f16((hi - lo) / qmax);
+      uint16_t z16 = zqo_f64_to_f16(lo);
+      if (!isfinite(zqo_f16_to_f64(s16)) || !isfinite(zqo_f16_to_f64(z16))) return ZQO_ERR_RANGE;
+      scales[r * gpr + g] = s16;
+      zeros[r * gpr + g] = z16;
+    }
+  }
+  return ZQO_OK;
+}
+
+int zqo_quantize_asym(const void* w, int w_dtype, int64_t n, int64_t k, int bits,
+                      const uint16_t* scales, const uint16_t* zeros, uint8_t* codes) {
+  int st = asym_shape_ok(n, k, bits);
+  if (st) return st;
+  if (w_dtype != ZQO_F16 && w_dtype != ZQO_BF16 && w_dtype != ZQO_F32)
+    return ZQO_ERR_INVALID_ARG;
+  const double qmax = (double)((1 << bits) - 1);
+  for (int64_t r = 0; r < n; ++r) {
+    for (int64_t c = 0; c < k; ++c) {
+      const int64_t si = r * (k / 128) + c / 128;
+      double s = zqo_f16_to_f64(scales[si]);
+      double z = zqo_f16_to_f64(zeros[si]);
+      double v = zqo_widen(w, w_dtype, r * k + c);
+      if (!isfinite(s) || !isfinite(z) || !isfinite(v)) return ZQO_ERR_RANGE;
+      double q = 0.0;
+      if (s != 0.0) {
+        q = nearbyint((v - z) / s); /* double arithmetic, round half to even */
+        if (q < 0.0) q = 0.0;
+        if (q > qmax) q = qmax;
+      }
+      codes[r * k + c] = (uint8_t)q;
+    }
+  }
+  return ZQO_OK;
+}
+
+int zqo_pack_u(const uint8_t* codes, int64_t n, int64_t k, int bits, uint8_t* packed) {
+  int st = shape_ok(n, k, bits, 0);
+  if (st) return st;
+  const int per = 8 / bits;
+  const unsigned qmax = (1u << bits) - 1u;
+  const int64_t row_bytes = k / per;
+  for (int64_t r = 0; r < n; ++r) {
+    for (int64_t j = 0; j < row_bytes; ++j) {
+      unsigned byte = 0;
+      for (int i = 0; i < per; ++i) {
+        unsigned q = codes[r * k + j * per + i];
+        if (q > qmax) return ZQO_ERR_RANGE;
+        byte |= q << (i * bits);
+      }
+      packed[r * row_bytes + j] = (uint8_t)byte;
+    }
+  }
+  return ZQO_OK;
+}
+
+/* unsigned code of element (r, c) read from the packed rows */
+static unsigned ucode_at(const uint8_t* packed, int bits, int64_t k, int64_t r, int64_t c) {
+  const int per = 8 / bits;
+  const int64_t row_bytes = k / per;
+  unsigned byte = packed[r * row_bytes + c / per];
+  return (byte >> ((c % per) * bits)) & ((1u << bits) - 1u);
+}
+
+void zqo_unpack_u(const uint8_t* packed, int64_t n, int64_t k, int bits, uint8_t* codes) {
+  for (int64_t r = 0; r < n; ++r)
+    for (int64_t c = 0; c < k; ++c)
+      codes[r * k + c] = (uint8_t)ucode_at(packed, bits, k, r, c);
+}
+
+void zqo_dequant_asym(const uint8_t* codes, int64_t n, int64_t k, const uint16_t* scales,
+                      const uint16_t* zeros, double* out) {
+  for (int64_t r = 0; r < n; ++r)
+    for (int64_t c = 0; c < k; ++c) {
+      const int64_t si = r * (k / 128) + c / 128;
+      out[r * k + c] = (double)codes[r * k + c] * zqo_f16_to_f64(scales[si]) + zqo_f16_to_f64(zeros[si]);
+    }
+}
+
+int zqo_gemm_asym(const uint8_t* packed, int bits, const uint16_t* scales, const uint16_t* zeros,
+                  int64_t n, int64_t k, const void* x, int x_dtype, int64_t m, int64_t ldx,
+                  double* y, int64_t ldy) {
+  int st = asym_shape_ok(n, k, bits);
+  if (st) return st;
+  if (x_dtype != ZQO_F16 && x_dtype != ZQO_BF16 && x_dtype != ZQO_F32)
+    return ZQO_ERR_INVALID_ARG;
+  if (m < 0 || ldx < k || ldy < n) return ZQO_ERR_INVALID_ARG;
+  for (int64_t mi = 0; mi < m; ++mi) {
+    for (int64_t r = 0; r < n; ++r) {
+      double acc = 0.0;
+      for (int64_t c = 0; c < k; ++c) {
+        const int64_t si = r * (k / 128) + c / 128;
+        double wdeq = (double)ucode_at(packed, bits, k, r, c) * zqo_f16_to_f64(scales[si]) +
+                      zqo_f16_to_f64(zeros[si]);
+        acc += zqo_widen(x, x_dtype, mi * ldx + c) * wdeq;
+      }
+      y[mi * ldy + r] = acc;
+    }
+  }
+  return ZQO_OK;
+}

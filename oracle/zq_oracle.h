@@ -94,6 +94,39 @@ int zqo_gemm(const uint8_t* packed, int bits, const uint16_t* scales, int group,
              int64_t n, int64_t k, const void* x, int x_dtype, int64_t m,
              int64_t ldx, double* y, int64_t ldy);
 
+/* ---------------------------------------------------------------------------
+ * Asymmetric variant: the quantizer the ZSE wiki prints in its section on the
+ * .zse model format (unsigned codes, one fp16 scale and one fp16 zero point per
+ * group of 128 weights, two 4-bit values per byte with the low nibble first).
+ * For b bits, qmax = 2^b - 1 (the wiki's formula is the b = 4 case, qmax = 15);
+ * b in {2, 4}, groups of 128 along K only.
+ *
+ * Readings where the page is silent:
+ *   - max and min are taken over the group's weights widened exactly to double;
+ *   - scale s16 = RNE_fp16((max - min) / qmax) and zero z16 = RNE_fp16(min),
+ *     both computed in double, stored as fp16 bit patterns;
+ *   - codes are computed from the stored s16 and z16:
+ *     q = clamp(rne((w - z16) / s16), 0, qmax) in double, ties to even;
+ *     s16 == 0 (max == min, or a span below the fp16 range) gives q = 0;
+ *   - w_deq = q * s16 + z16, exact in double;
+ *   - non-finite w, or a scale or zero beyond the fp16 range -> ZQO_ERR_RANGE.
+ * Scales and zeros share the layout of the symmetric group scales: [N][K/128].
+ */
+int zqo_compute_scales_zeros(const void* w, int w_dtype, int64_t n, int64_t k, int bits,
+                             uint16_t* scales, uint16_t* zeros);
+int zqo_quantize_asym(const void* w, int w_dtype, int64_t n, int64_t k, int bits,
+                      const uint16_t* scales, const uint16_t* zeros, uint8_t* codes);
+/* Packing of unsigned codes in [0, 2^b - 1] (same bit positions as zqo_pack;
+ * codes out of range -> ZQO_ERR_RANGE), and its inverse (no sign extension). */
+int  zqo_pack_u(const uint8_t* codes, int64_t n, int64_t k, int bits, uint8_t* packed);
+void zqo_unpack_u(const uint8_t* packed, int64_t n, int64_t k, int bits, uint8_t* codes);
+void zqo_dequant_asym(const uint8_t* codes, int64_t n, int64_t k, const uint16_t* scales,
+                      const uint16_t* zeros, double* out);
+/* y[m][n] = sum over k ascending of double(x[m][k]) * (q[n][k] * s + z). */
+int zqo_gemm_asym(const uint8_t* packed, int bits, const uint16_t* scales, const uint16_t* zeros,
+                  int64_t n, int64_t k, const void* x, int x_dtype, int64_t m, int64_t ldx,
+                  double* y, int64_t ldy);
+
 #ifdef __cplusplus
 }
 #endif

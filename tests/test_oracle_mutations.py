@@ -39,6 +39,16 @@ MUTATIONS = [
      "acc += zqo_widen(x, x_dtype, (r % (m > 0 ? m : 1)) * ldx + c) * wdeq;"),
     ("bf16 exponent bias off by one",
      "v = ldexp((double)(128 + f), e - 127 - 7);", "v = ldexp((double)(128 + f), e - 126 - 7);"),
+    ("asymmetric: zero point dropped from the product",
+     "* zqo_f16_to_f64(scales[si]) +\n                      zqo_f16_to_f64(zeros[si]);",
+     "* zqo_f16_to_f64(scales[si]);"),
+    ("asymmetric: scale divides by 2^b instead of 2^b - 1",
+     "uint16_t s16 = zqo_f64_to_f16((hi - lo) / qmax);", "uint16_t s16 = zqo_f64_to_f16((hi - lo) / (qmax + 1));"),
+    ("asymmetric: lowest code clamped to 1",
+     "if (q < 0.0) q = 0.0;", "if (q < 1.0) q = 1.0;"),
+    ("asymmetric: unsigned field masked one bit short",
+     "return (byte >> ((c % per) * bits)) & ((1u << bits) - 1u);",
+     "return (byte >> ((c % per) * bits)) & ((1u << (bits - 1)) - 1u);"),
 ]
 
 
@@ -57,8 +67,8 @@ def test_pins_catch_planted_mistake(tmp_path, name, old, new):
     shutil.copy(os.path.join(ROOT, "pytest.ini"), dst / "pytest.ini")
     c = dst / "oracle" / "zq_oracle.c"
     text = c.read_text()
-    assert text.count(old) == 1, f"mutation site not found: {old}"
-    c.write_text(text.replace(old, new))
+    assert old in text, f"mutation site not found: {old}"
+    c.write_text(text.replace(old, new, 1))  # the first site (the symmetric functions come first)
     env = dict(os.environ, PYTHONPATH=str(dst))
     r = subprocess.run([sys.executable, "-m", "pytest", "tests/test_oracle_pins.py", "-x", "-q",
                         "-p", "no:cacheprovider"], cwd=dst, env=env, capture_output=True, text=True,

@@ -382,3 +382,122 @@ def test_gemm_rows_matches_full_gemm():
     full = O.gemm(p, 4, s, 128, n, k, x, "f16")
     rows = np.array([0, 7, 19])
     assert np.array_equal(O.gemm_rows(p, 4, s, 128, n, k, x, "f16", rows), full[:, rows])
+
+
+# ---------------------------------------------------------------------------
+# asymmetric variant (unsigned codes, fp16 scale and zero per 128-group), the
+# quantizer of the ZSE wiki's section on the .zse model format
+
+
+def test_asym_closed_form_integer_grid():
+    """weights 0..15 in every group: scale (15 - 0) / 15 = 1, zero 0, codes = weights"""
+    w = np.tile(np.arange(16, dtype=np.float32), 16).reshape(2, 128)
+    s, z = O.compute_scales_zeros(w, "f32", 4)
+    assert np.all(s == 0x3C00) and np.all(z == 0)
+    q = O.quantize_asym(w, "f32", 4, s, z)
+    assert np.array_equal(q, w.astype(np.uint8))
+    assert np.array_equal(O.dequant_asym(q, s, z), w.astype(np.float64))
+
+
+def test_asym_worked_scale_and_zero_bits():
+    """min -1, max 2: scale 3/15 = 0.2 -> fp16 0x3266 (0.199951171875), zero -1 -> 0xBC00"""
+    w = (-1.0 + 3.0 * np.arange(128) / 127).astype(np.float32).reshape(1, 128)
+    w[0, 0], w[0, -1] = -1.0, 2.0
+    s, z = O.compute_scales_zeros(w, "f32", 4)
+    assert s[0] == 0x3266 and O.f16_to_f64(int(s[0])) == 0.199951171875
+    assert z[0] == 0xBC00
+    # INT2: scale 3/3 = 1
+    s2, z2 = O.compute_scales_zeros(w, "f32", 2)
+    assert s2[0] == 0x3C00 and z2[0] == 0xBC00
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+def test_asym_codes_are_nearest_grid_points(bits):
+    """brute force: each code minimises |w - (z + q s)| over q in [0, 2^b - 1]; ties to even q"""
+    g = synth.rng(71 + bits)
+    w = (g.standard_normal((6, 256)) * np.array([[1], [0.01], [100], [3], [1e-3], [7]])).astype(np.float32)
+    s, z = O.compute_scales_zeros(w, "f32", bits)
+    q = O.quantize_asym(w, "f32", bits, s, z)
+    qmax = (1 << bits) - 1
+    grid = np.arange(qmax + 1, dtype=np.float64)
+    for r in range(w.shape[0]):
+        for c in range(w.shape[1]):
+            si = r * 2 + c // 128
+            sv, zv = O.f16_to_f64(int(s[si])), O.f16_to_f64(int(z[si]))
+            d = np.abs(float(w[r, c]) - (zv + grid * sv))
+            best = np.flatnonzero(d == d.min())
+            expect = best[0] if len(best) == 1 else [b for b in best if b % 2 == 0][0]
+            assert q[r, c] == expect, (r, c)
+
+
+def test_asym_error_bound_and_constant_group():
+    g = synth.rng(5)
+    w = g.standard_normal((8, 384)).astype(np.float32)
+    w[3, 128:256] = 0.7  # a constant group: scale 0, codes 0, w_deq = fp16(0.7)
+    s, z = O.compute_scales_zeros(w, "f32", 4)
+    q = O.quantize_asym(w, "f32", 4, s, z)
+    wd = O.dequant_asym(q, s, z)
+    sv = np.array([O.f16_to_f64(int(v)) for v in s]).reshape(8, 3).repeat(128, axis=1)
+    assert s[3 * 3 + 1] == 0 and np.all(q[3, 128:256] == 0)
+    assert np.all(wd[3, 128:256] == O.f16_to_f64(O.f64_to_f16(0.7)))
+    mask = sv > 0
+    assert np.all(np.abs(w.astype(np.float64) - wd)[mask] <= sv[mask] / 2 * (1 + 1e-9))
+
+
+def test_asym_pack_u_round_trip_and_hand_examples():
+    for bits in (2, 4):
+        per = 8 // bits
+        b = np.arange(256, dtype=np.uint8).reshape(1, 256)
+        q = O.unpack_u(b, 1, 256 * per, bits)
+        assert q.max() == (1 << bits) - 1
+        assert np.array_equal(O.pack_u(q, bits), b)
+    assert O.pack_u(np.array([[1, 15]], dtype=np.uint8), 4)[0, 0] == 0xF1
+    assert O.pack_u(np.array([[1, 2, 0, 3]], dtype=np.uint8), 2)[0, 0] == 0xC9
+    with pytest.raises(O.OracleError):
+        O.pack_u(np.array([[16, 0]], dtype=np.uint8), 4)
+
+
+@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("xdt", ["f16", "bf16"])
+def test_asym_gemm_equals_dense_matmul(bits, xdt):
+    g = synth.rng(90 + bits)
+    n, k, m = 9, 384, 3
+    w = g.standard_normal((n, k)).astype(np.float32)
+    s, z = O.compute_scales_zeros(w, "f32", bits)
+    q = O.quantize_asym(w, "f32", bits, s, z)
+    p = O.pack_u(q, bits)
+    x = synth.normal(g, (m, k), xdt)
+    x64 = torch.from_numpy(x.view(np.int16)).view(torch.bfloat16).double().numpy() if xdt == "bf16" \
+        else x.astype(np.float64)
+    ref = x64 @ O.dequant_asym(O.unpack_u(p, n, k, bits), s, z).T
+    np.testing.assert_allclose(O.gemm_asym(p, bits, s, z, n, k, x, xdt), ref, rtol=1e-12, atol=1e-12)
+
+
+def test_asym_gemm_reduces_to_symmetric_plus_zero_term():
+    """q s + z = (q - 8) s + (z + 8 s): the asymmetric product is the pinned
+    symmetric one on shifted codes plus one term per group; exact on integers"""
+    g = synth.rng(33)
+    n, k, m, bits = 7, 256, 4, 4
+    q = g.integers(0, 16, size=(n, k)).astype(np.uint8)
+    s = np.where(g.random(n * 2) < 0.5, 0x3800, 0x3C00).astype(np.uint16)   # 0.5 or 1
+    z = np.array([O.f64_to_f16(v) for v in g.integers(-6, 6, n * 2)], dtype=np.uint16)
+    x = g.integers(-4, 5, size=(m, k)).astype(np.float16)
+    y = O.gemm_asym(O.pack_u(q, bits), bits, s, z, n, k, x, "f16")
+    ys = O.gemm(O.pack(q.astype(np.int16) - 8, bits), bits, s, 128, n, k, x, "f16")
+    sv = np.array([O.f16_to_f64(int(v)) for v in s]).reshape(n, 2)
+    zv = np.array([O.f16_to_f64(int(v)) for v in z]).reshape(n, 2)
+    xg = x.astype(np.float64).reshape(m, 2, 128).sum(2)          # [m][group]
+    assert np.array_equal(y, ys + xg @ (zv + 8 * sv).T)
+
+
+def test_asym_range_errors():
+    w = np.zeros((1, 128), dtype=np.float32)
+    w[0, 5] = np.inf
+    with pytest.raises(O.OracleError):
+        O.compute_scales_zeros(w, "f32", 4)
+    w = np.zeros((1, 128), dtype=np.float32)
+    w[0, 0], w[0, 1] = -6e5, 6e5  # zero beyond fp16
+    with pytest.raises(O.OracleError):
+        O.compute_scales_zeros(w, "f32", 4)
+    with pytest.raises(O.OracleError):
+        O.compute_scales_zeros(np.zeros((1, 100), np.float32), "f32", 4)

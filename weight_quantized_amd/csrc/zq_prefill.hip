@@ -32,7 +32,7 @@
 
 namespace zq {
 
-constexpr int P2_BM = 256, P2_BN = 256, P2_BK = 64, P2_THREADS = 512;
+constexpr int P2_BM = 256, P2_BN = 256, P2_BK = 64;
 constexpr int P2_TILE = 256 * 128;            // bytes of one 256-row x 64-k 16-bit activation tile
 constexpr int P2_LDS = 2 * P2_TILE + 256 * 4;  // two stages + row sums
 
@@ -100,53 +100,61 @@ __device__ __forceinline__ u4 p2_bfrag(const u4 (&c)[2], int kk) {
   }
 }
 
-template <int XT, int BITS>
-__global__ __launch_bounds__(P2_THREADS) void gemm_prefill2_kernel(
+// WGM x WGN waves; wave (wm, wn) computes rows 256/WGM * wm.. and columns
+// 256/WGN * wn.. of the tile as FI x FJ MFMA 32x32 tiles.
+template <int XT, int BITS, int WGM, int WGN>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_prefill2_kernel(
     const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales, int64_t n, int64_t k,
     const uint16_t* __restrict__ x, int64_t m, int64_t ldx, void* __restrict__ y, int64_t ldy, int yt) {
   extern __shared__ __align__(16) uint8_t smem[];
+  constexpr int NT = 64 * WGM * WGN;
+  constexpr int TM = P2_BM / WGM, TN = P2_BN / WGN, FI = TM / 32, FJ = TN / 32;
+  constexpr int SPT = 1024 / NT;            // 16-k activation spans per thread per step
   constexpr int CB = 8 * BITS;              // code bytes of one row per 64-k step
   constexpr int NB = BITS == 8 ? 2 : 1;     // 16-byte code loads per lane per fragment
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 2, wn = wave & 3;
+  const int wm = wave / WGN, wn = wave % WGN;
   const int g = lane >> 5;
   const int64_t m0 = (int64_t)blockIdx.y * P2_BM, n0 = (int64_t)blockIdx.x * P2_BN;
   const int64_t rowbytes = k * BITS / 8;
   const int64_t KT = k / P2_BK;
   float* rowsum = reinterpret_cast<float*>(smem + 2 * P2_TILE);
 
-  // activation staging: spans (row = s/4, 16-k span s%4), s = it*512 + tid
-  const uint16_t* xrow[2];
+  // activation staging: spans (row = s/4, 16-k span s%4), s = it*NT + tid
+  const uint16_t* xrow[SPT];
+  bool xlive[SPT];
 #pragma unroll
-  for (int it = 0; it < 2; ++it) {
-    const int s = it * 512 + tid;
+  for (int it = 0; it < SPT; ++it) {
+    const int s = it * NT + tid;
     const int64_t r = m0 + (s >> 2);
     xrow[it] = x + (r < m ? r : m - 1) * ldx + 16 * (s & 3);
+    xlive[it] = r < m;
   }
-  const bool xlive0 = m0 + (tid >> 2) < m, xlive1 = m0 + 128 + (tid >> 2) < m;
-  // weight fragments of this wave: rows n0 + 64 wn + 32 j + lane % 32, bytes
+  // weight fragments of this wave: rows n0 + TN wn + 32 j + lane % 32, bytes
   // CB/2 * g of each step
-  const uint8_t* wfr[2];
+  const uint8_t* wfr[FJ];
 #pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int64_t r = n0 + wn * 64 + 32 * j + (lane & 31);
+  for (int j = 0; j < FJ; ++j) {
+    const int64_t r = n0 + wn * TN + 32 * j + (lane & 31);
     wfr[j] = packed + (r < n ? r : n - 1) * rowbytes + (CB / 2) * g;
   }
 
   // two register sets: tile kt + 2 is loaded while tile kt computes
-  u4 xa0[2][2], xa1[2][2], wb0[2][2], wb1[2][2];
-  float rs[2] = {0.f, 0.f};
-  auto load_x = [&](int64_t kt, u4 (&xa)[2][2]) __attribute__((always_inline)) {
+  u4 xa0[SPT][2], xa1[SPT][2], wb0[FJ][2], wb1[FJ][2];
+  float rs[SPT];
 #pragma unroll
-    for (int it = 0; it < 2; ++it) {
+  for (int it = 0; it < SPT; ++it) rs[it] = 0.f;
+  auto load_x = [&](int64_t kt, u4 (&xa)[SPT][2]) __attribute__((always_inline)) {
+#pragma unroll
+    for (int it = 0; it < SPT; ++it) {
       const u4* p = reinterpret_cast<const u4*>(xrow[it] + kt * P2_BK);
       xa[it][0] = *to_global(p);
       xa[it][1] = *to_global(p + 1);
     }
   };
-  auto load_w = [&](int64_t kt, u4 (&wb)[2][2]) __attribute__((always_inline)) {
+  auto load_w = [&](int64_t kt, u4 (&wb)[FJ][2]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < 2; ++j) {
+    for (int j = 0; j < FJ; ++j) {
       const uint8_t* q = wfr[j] + kt * CB;
       if constexpr (BITS == 2) {
         const u2 t = __builtin_nontemporal_load(to_global(reinterpret_cast<const u2*>(q)));
@@ -158,58 +166,56 @@ __global__ __launch_bounds__(P2_THREADS) void gemm_prefill2_kernel(
     }
   };
   // stage activation span `it` of a tile into LDS stage st
-  auto stage_span = [&](uint8_t* st, const u4 (&xa)[2][2], int it) __attribute__((always_inline)) {
-    const bool live = it == 0 ? xlive0 : xlive1;
-    const int s = it * 512 + tid, r = s >> 2, sp = s & 3;
+  auto stage_span = [&](uint8_t* st, const u4 (&xa)[SPT][2], int it) __attribute__((always_inline)) {
+    const int s = it * NT + tid, r = s >> 2, sp = s & 3;
     u4 p0 = xa[it][0], p1 = xa[it][1];
-    if (!live) p0 = p1 = u4{0u, 0u, 0u, 0u};
+    if (!xlive[it]) p0 = p1 = u4{0u, 0u, 0u, 0u};
     rs[it] = p2_sum8<XT>(p1, p2_sum8<XT>(p0, rs[it]));
     u4 s0, s1;
     p2_perm<BITS>(p0, p1, s0, s1);
     *reinterpret_cast<u4*>(st + p2_off(r, 2 * sp)) = s0;
     *reinterpret_cast<u4*>(st + p2_off(r, 2 * sp + 1)) = s1;
   };
-  auto stage = [&](uint8_t* st, const u4 (&xa)[2][2]) __attribute__((always_inline)) {
-    stage_span(st, xa, 0);
-    stage_span(st, xa, 1);
-  };
 
-  f16v acc[4][2];
+  f16v acc[FI][FJ];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < FI; ++i)
 #pragma unroll
-    for (int j = 0; j < 2; ++j) acc[i][j] = f16v{};
+    for (int j = 0; j < FJ; ++j) acc[i][j] = f16v{};
 
-  auto read_a = [&](const uint8_t* cur, int kk, u4 (&a)[4]) __attribute__((always_inline)) {
+  auto read_a = [&](const uint8_t* cur, int kk, u4 (&a)[FI]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      a[i] = *reinterpret_cast<const u4*>(cur + p2_off(wm * 128 + 32 * i + (lane & 31), 4 * g + kk));
+    for (int i = 0; i < FI; ++i)
+      a[i] = *reinterpret_cast<const u4*>(cur + p2_off(wm * TM + 32 * i + (lane & 31), 4 * g + kk));
   };
   // one K step: the tile in LDS stage kt & 1 with weight codes `wb`. The
   // fragments of step kk + 1 are read before the MFMAs of step kk; the
   // activations of tile kt + 1 (`nxa`) are staged into the other stage
   // between the MFMA steps.
-  auto kstep = [&](int64_t kt, const u4 (&wb)[2][2], const u4 (&nxa)[2][2], u4 (&lxa)[2][2], u4 (&lwb)[2][2])
-      __attribute__((always_inline)) {
+  auto kstep = [&](int64_t kt, const u4 (&wb)[FJ][2], const u4 (&nxa)[SPT][2], u4 (&lxa)[SPT][2],
+                   u4 (&lwb)[FJ][2]) __attribute__((always_inline)) {
     const uint8_t* cur = smem + (kt & 1) * P2_TILE;
     uint8_t* nxt = smem + ((kt + 1) & 1) * P2_TILE;
     const bool stage_next = kt + 1 < KT;
     if (kt + 2 < KT) load_x(kt + 2, lxa);  // tile kt's activations are already staged
-    u4 a0[4], a1[4];
+    u4 a0[FI], a1[FI];
     read_a(cur, 0, a0);
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
-      u4 (&a)[4] = (kk & 1) ? a1 : a0;
-      u4 (&an)[4] = (kk & 1) ? a0 : a1;
+      u4 (&a)[FI] = (kk & 1) ? a1 : a0;
+      u4 (&an)[FI] = (kk & 1) ? a0 : a1;
       if (kk < 3) read_a(cur, kk + 1, an);
-      u4 b[2];
+      u4 b[FJ];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) b[j] = p2_bfrag<XT, BITS>(wb[j], kk);
+      for (int j = 0; j < FJ; ++j) b[j] = p2_bfrag<XT, BITS>(wb[j], kk);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < FI; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = p2_mfma<XT>(a[i], b[j], acc[i][j]);
-      if (stage_next && (kk & 1)) stage_span(nxt, nxa, kk >> 1);
+        for (int j = 0; j < FJ; ++j) acc[i][j] = p2_mfma<XT>(a[i], b[j], acc[i][j]);
+      // spread this thread's spans over the 4 MFMA steps
+#pragma unroll
+      for (int it = 0; it < SPT; ++it)
+        if (stage_next && (it * 4) / SPT == kk) stage_span(nxt, nxa, it);
       __builtin_amdgcn_sched_barrier(0);
     }
     if (kt + 2 < KT) load_w(kt + 2, lwb);  // tile kt's codes are consumed
@@ -222,7 +228,8 @@ __global__ __launch_bounds__(P2_THREADS) void gemm_prefill2_kernel(
     load_x(1, xa1);
     load_w(1, wb1);
   }
-  stage(smem, xa0);
+#pragma unroll
+  for (int it = 0; it < SPT; ++it) stage_span(smem, xa0, it);
   __syncthreads();
   for (int64_t kt = 0; kt < KT; kt += 2) {
     kstep(kt, wb0, xa1, xa0, wb0);  // compute tile kt (codes in set 0); stage kt+1 (set 1); load kt+2 into set 0
@@ -231,11 +238,11 @@ __global__ __launch_bounds__(P2_THREADS) void gemm_prefill2_kernel(
 
   // row sums: the 4 spans of a row are 4 consecutive threads
 #pragma unroll
-  for (int it = 0; it < 2; ++it) {
+  for (int it = 0; it < SPT; ++it) {
     float v = rs[it];
     v += __shfl_xor(v, 1, 64);
     v += __shfl_xor(v, 2, 64);
-    if ((tid & 3) == 0) rowsum[it * 128 + (tid >> 2)] = v;
+    if ((tid & 3) == 0) rowsum[it * (NT / 4) + (tid >> 2)] = v;
   }
   __syncthreads();
 
@@ -243,15 +250,15 @@ __global__ __launch_bounds__(P2_THREADS) void gemm_prefill2_kernel(
   const float s = f16_bits_to_float(scales[0]);
   // D layout of 32x32: value r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < FI; ++i) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int rl = wm * 128 + 32 * i + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
+      const int rl = wm * TM + 32 * i + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
       const int64_t row = m0 + rl;
       const float corr = Dc::BIAS * rowsum[rl];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const int64_t col = n0 + wn * 64 + 32 * j + (lane & 31);
+      for (int j = 0; j < FJ; ++j) {
+        const int64_t col = n0 + wn * TN + 32 * j + (lane & 31);
         if (row < m && col < n) store_y(y, row * ldy + col, s * (acc[i][j][r] - corr), yt);
       }
     }
@@ -264,14 +271,20 @@ bool gemm_prefill2_supported(const GemmArgs& a) {
   return true;
 }
 
+#ifndef ZQ_P2_WGM
+#define ZQ_P2_WGM 2
+#define ZQ_P2_WGN 4
+#endif
+
 template <int XT, int BITS>
 static hipError_t p2_launch(const GemmArgs& a) {
-  const void* fn = reinterpret_cast<const void*>(&gemm_prefill2_kernel<XT, BITS>);
+  constexpr int WGM = ZQ_P2_WGM, WGN = ZQ_P2_WGN;
+  const void* fn = reinterpret_cast<const void*>(&gemm_prefill2_kernel<XT, BITS, WGM, WGN>);
   hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, P2_LDS);
   if (e != hipSuccess) return e;
   const dim3 grid((unsigned)((a.n + P2_BN - 1) / P2_BN), (unsigned)((a.m + P2_BM - 1) / P2_BM));
-  hipLaunchKernelGGL((gemm_prefill2_kernel<XT, BITS>), grid, dim3(P2_THREADS), P2_LDS, a.stream, a.packed,
-                     a.scales, a.n, a.k, a.x, a.m, a.ldx, a.y, a.ldy, a.yt);
+  hipLaunchKernelGGL((gemm_prefill2_kernel<XT, BITS, WGM, WGN>), grid, dim3(64 * WGM * WGN), P2_LDS, a.stream,
+                     a.packed, a.scales, a.n, a.k, a.x, a.m, a.ldx, a.y, a.ldy, a.yt);
   return hipGetLastError();
 }
 
