@@ -14,6 +14,8 @@ Prints one JSON line. Other workloads (--config):
   gemv-512             single 512 x 512 INT4 GEMV, per-tensor scale fp16(0.02)
   qwen7b-batch --m M   the 7B stack at M in {1,4,8,16,32}, bf16 activations
   qwen32b-decode       64 layers of Qwen2.5-32B projection shapes, M = 1
+  qwen7b-decode-asym   the 7B decode stack with asymmetric INT4 weights (unsigned
+                       codes, fp16 scale and zero point per 128-group)
   qwen7b-prefill       7B stack, bits per layer from {2,4,8}, per-tensor scales,
                        M = 2048 bf16 tokens (MFMA-bound: TFLOP/s)
   hbm-copy             a plain 1 GiB device-to-device copy (torch), the
@@ -65,7 +67,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", default="qwen7b-decode",
                    choices=["gemv-512", "qwen7b-decode", "qwen7b-batch", "qwen32b-decode", "qwen7b-prefill",
-                            "hbm-copy"])
+                            "qwen7b-decode-asym", "hbm-copy"])
     p.add_argument("--m", type=int, default=None, help="activation rows (qwen7b-batch)")
     p.add_argument("--launch", default=None, choices=["plan", "graph", "eager"],
                    help="plan: one resident launch per step (m <= 32, the default there); "
@@ -91,7 +93,7 @@ class Stack:
         dev = torch.device("cuda:0")
         if cfg == "gemv-512":
             shapes, L, bits_of, group, xdt, self.m = [("w", 512, 512)], 1, (lambda l: 4), 0, "f16", 1
-        elif cfg == "qwen7b-decode":
+        elif cfg in ("qwen7b-decode", "qwen7b-decode-asym"):
             shapes, L, bits_of, group, xdt, self.m = synth.QWEN25_7B, 28, (lambda l: 4), 128, "f16", 1
         elif cfg == "qwen7b-batch":
             shapes, L, bits_of, group, xdt, self.m = synth.QWEN25_7B, 28, (lambda l: 4), 128, "bf16", m or 8
@@ -119,7 +121,8 @@ class Stack:
                     scales = synth.device_scales_abs_normal(ns, 2000003 * seed, dev)
                 x = synth.device_normal((self.m, k), xdt, 3000003 * seed, dev)
                 y = torch.empty((self.m, n), dtype=torch.float32, device=dev)
-                W = zq.ZqWeight(bits, group, n, k, packed, scales)
+                zeros = synth.device_zeros_normal(ns, 4000003 * seed, dev) if cfg.endswith("-asym") else None
+                W = zq.ZqWeight(bits, group, n, k, packed, scales, zeros)
                 self.launches.append((W, x, y))
                 self.weight_bytes += W.nbytes
                 self.flops += 2 * self.m * n * k
@@ -216,13 +219,18 @@ def cpu_baseline(stack: Stack, torch, synth, budget_s: float = 12.0):
                 r0, r1 = int(bounds[t]), int(bounds[t + 1])
                 if r1 > r0:
                     s_rows = sc if W.group == 0 else sc.reshape(W.n, -1)[r0:r1]
-                    jobs.append((p[r0:r1], W.bits, s_rows, W.group, r1 - r0, W.k, xh, xdt))
+                    z_rows = None if W.zeros is None else \
+                        W.zeros.view(torch.int16).cpu().numpy().view(np.uint16).reshape(W.n, -1)[r0:r1]
+                    jobs.append((p[r0:r1], W.bits, s_rows, z_rows, W.group, r1 - r0, W.k, xh, xdt))
         # one thread per core; each runs its share of rows of every projection
         per_thread = [jobs[i::threads] for i in range(threads)]
 
         def work(js):
-            for (pp, bits, ss, grp, n, k, xh_, xd) in js:
-                O.gemm(pp, bits, ss, grp, n, k, xh_, xd)
+            for (pp, bits, ss, zz, grp, n, k, xh_, xd) in js:
+                if zz is None:
+                    O.gemm(pp, bits, ss, grp, n, k, xh_, xd)
+                else:
+                    O.gemm_asym(pp, bits, ss, zz, n, k, xh_, xd)
 
         ths = [threading.Thread(target=work, args=(js,)) for js in per_thread]
         t0 = time.perf_counter()
@@ -379,6 +387,8 @@ def main():
     out["config"] = {"workload": {
         "gemv-512": "single 512x512 INT4 GEMV, per-tensor fp16 scale 0.02, M=1, fp16 x",
         "qwen7b-decode": "Qwen2.5-7B-shaped decode stack: 28 layers x 7 projections, M=1, INT4 group-128, fp16 x",
+        "qwen7b-decode-asym": "Qwen2.5-7B-shaped decode stack: 28 layers x 7 projections, M=1, asymmetric INT4 "
+                              "(fp16 scale and zero point per 128-group), fp16 x",
         "qwen7b-batch": f"Qwen2.5-7B-shaped stack, M={stack.m}, INT4 group-128, bf16 x",
         "qwen32b-decode": "Qwen2.5-32B-shaped decode stack: 64 layers x 7 projections, M=1, INT4 group-128, fp16 x",
         "qwen7b-prefill": "Qwen2.5-7B-shaped prefill stack, per-layer INT2/INT4/INT8, per-tensor scale, M=2048, bf16 x",

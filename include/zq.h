@@ -88,6 +88,11 @@ typedef struct zq_weight {
   int64_t k;              /* input features */
   const void* packed;     /* device, zq_packed_bytes(bits, n, k) bytes */
   const uint16_t* scales; /* device, zq_num_scales(group, n, k) fp16 patterns */
+  const uint16_t* zeros;  /* NULL: symmetric signed codes (above). Non-NULL:
+                           * asymmetric weights -- device, n * (k / 128) fp16
+                           * zero points laid out like the scales; codes are
+                           * unsigned in [0, 2^b - 1] and w_deq = q * s + z;
+                           * bits 2 or 4 and group 128 only. */
 } zq_weight;
 
 /* Bytes of packed codes: n * k * bits / 8. Returns 0 for unsupported bits. */
@@ -124,6 +129,35 @@ int64_t zq_num_scales(int group, int64_t n, int64_t k);
  * range; packed_out / scales_out contents are then unspecified. It allocates
  * and frees a few bytes of device memory for the error flag.
  */
+/*
+ * zq_pack_asym -- quantize and pack one weight matrix as asymmetric codes,
+ * the .zse format's own quantizer. [wiki, section "Формат модели .zse":
+ * asymmetric INT4 with a scale and a zero point per group of 128 weights,
+ * both stored as fp16; scale = (max - min) / 15, zero = min, codes clamped to
+ * [0, 15]; two values per byte, low nibble first.] For b bits the divisor is
+ * qmax = 2^b - 1 (b in {2, 4}); the group is always 128 along K.
+ *   w          device, [n][k] row-major, dtype w_dtype:
+ *              ZQ_I8  -- ready-made unsigned codes in [0, qmax] (ZQ_ERR_RANGE
+ *                        otherwise): pure bit packing; scales_in and zeros_in
+ *                        are required and copied to scales_out / zeros_out
+ *                        when those are non-NULL.
+ *              ZQ_F16 / ZQ_BF16 / ZQ_F32 -- float weights to quantize.
+ *   scales_in, zeros_in  device, both NULL or both n * (k / 128) fp16
+ *              patterns. NULL with float weights: per group,
+ *                s = fp16_round_nearest_even((max - min) / qmax),
+ *                z = fp16_round_nearest_even(min);
+ *   codes      q = clamp(round_half_even((w - z) / s), 0, qmax) with the
+ *              stored fp16 s and z, in double; s == 0 gives q = 0.
+ *   packed_out device, zq_packed_bytes(bits, n, k) bytes, written.
+ *   scales_out, zeros_out  device, n * (k / 128) fp16 patterns each, written.
+ * Synchronous, like zq_pack. ZQ_ERR_RANGE for a non-finite weight, or a scale
+ * or zero beyond the fp16 range. The result is used through a zq_weight whose
+ * `zeros` points at the zero points.
+ */
+zq_status zq_pack_asym(const void* w, zq_dtype w_dtype, int64_t n, int64_t k, int bits,
+                       const uint16_t* scales_in, const uint16_t* zeros_in, void* packed_out,
+                       uint16_t* scales_out, uint16_t* zeros_out, void* stream);
+
 zq_status zq_pack(const void* w, zq_dtype w_dtype, int64_t n, int64_t k, int bits,
                   int group, const uint16_t* scales_in, void* packed_out,
                   uint16_t* scales_out, void* stream);
@@ -132,9 +166,10 @@ zq_status zq_pack(const void* w, zq_dtype w_dtype, int64_t n, int64_t k, int bit
  * zq_unpack -- decode a packed matrix. [wiki, section "Компилятор GPU-ядер":
  * the unpack_int4 intrinsic; this is its signed form for 2, 4 and 8 bits.]
  *   out  device, [n][k] row-major of out_dtype:
- *        ZQ_I8  -- the integer codes, sign-extended;
- *        ZQ_F32 -- q * s exactly;
- *        ZQ_F16 / ZQ_BF16 -- q * s rounded to nearest even.
+ *        ZQ_I8  -- the integer codes, sign-extended (asymmetric weights: the
+ *                  unsigned codes, 0 .. 2^b - 1);
+ *        ZQ_F32 -- q * s exactly (asymmetric: q * s + z, rounded once);
+ *        ZQ_F16 / ZQ_BF16 -- q * s (q * s + z) rounded to nearest even.
  * Asynchronous on `stream`.
  */
 zq_status zq_unpack(const zq_weight* W, void* out, zq_dtype out_dtype, void* stream);
@@ -162,7 +197,8 @@ zq_status zq_gemv(const zq_weight* W, const void* x, zq_dtype x_dtype, void* y,
  *   Y       device, m rows of n elements, row stride ldy >= n, dtype ZQ_F32,
  *           ZQ_F16 or ZQ_BF16.
  * Kernels by shape (all give results within the same tolerance of the exact
- * sums; integer-valued inputs give exact sums on every path):
+ * sums; integer-valued inputs give exact sums on every path). Asymmetric
+ * weights run on the m <= 4 vector-ALU kernel or the general kernel:
  *   m = 1 (and m <= 4 for INT2/INT8): a vector-ALU kernel that streams the
  *     codes once with 128-bit loads;
  *   m = 2..32, INT4, k a multiple of 512, 16-byte aligned codes and

@@ -122,3 +122,24 @@ def test_gemv_and_unpack_validation(L):
 ])
 def test_pack_validation_without_device(L, args, status):
     assert L.zq_pack(*args, None) == status
+
+
+@pytest.mark.parametrize("args,status", [
+    ((0x1000, zq.F32, 4, 256, 8, None, None, 0x2000, 0x3000, 0x4000), zq.ERR_UNSUPPORTED),   # INT8
+    ((0x1000, zq.F32, 4, 200, 4, None, None, 0x2000, 0x3000, 0x4000), zq.ERR_UNSUPPORTED),   # k % 128
+    ((0x1000, 7, 4, 256, 4, None, None, 0x2000, 0x3000, 0x4000), zq.ERR_INVALID_ARG),        # dtype
+    ((0, zq.F32, 4, 256, 4, None, None, 0x2000, 0x3000, 0x4000), zq.ERR_INVALID_ARG),        # null w
+    ((0x1000, zq.F32, 4, 256, 4, 0x5000, None, 0x2000, 0x3000, 0x4000), zq.ERR_INVALID_ARG),  # half given
+    ((0x1000, zq.F32, 4, 256, 4, None, None, 0x2000, 0x3000, None), zq.ERR_INVALID_ARG),     # no zeros out
+    ((0x1000, zq.I8, 4, 256, 4, None, None, 0x2000, None, None), zq.ERR_INVALID_ARG),        # codes, no s/z
+])
+def test_pack_asym_validation_without_device(L, args, status):
+    assert L.zq_pack_asym(*args, None) == status
+
+
+def test_asymmetric_weight_validation(L):
+    for bits, group in ((8, 128), (4, 0)):
+        w = W(bits=bits, group=group)
+        w.zeros = 0x7000
+        assert L.zq_unpack(ctypes.byref(w), 0x3000, zq.F32, None) == zq.ERR_UNSUPPORTED
+        assert gemm(L, w) == zq.ERR_UNSUPPORTED

@@ -3,6 +3,7 @@ times, on sampled outputs: for every product of the step, a few weight rows
 and activation rows are copied back and recomputed by the fp64 oracle.
 
     Qwen2.5-7B decode stack   (28 layers x 7, M = 1, INT4 g128, fp16 x), plan
+    Qwen2.5-7B decode stack with asymmetric INT4 weights, plan
     Qwen2.5-32B decode stack  (64 layers x 7, M = 1), plan
     7B stack, M = 8 and 32 (bf16 x), plan (MFMA batched-decode kernel)
     7B prefill stack (per-layer INT2/4/8, per-tensor scale, M = 2048, bf16 x),
@@ -73,14 +74,21 @@ def check_sampled(stack, n_rows=6, m_rows=None, seed=0):
         if W.group:
             sc = sc.reshape(W.n, -1)[rows]
         xs = x[torch.from_numpy(ms).to(x.device)].view(torch.int16).cpu().numpy().view(np.uint16)
-        yref = O.gemm(p, W.bits, sc, W.group, len(rows), W.k, xs, xdt)
+        zr = None if W.zeros is None else \
+            W.zeros.view(torch.int16).cpu().numpy().view(np.uint16).reshape(W.n, -1)[rows]
+        if zr is None:
+            yref = O.gemm(p, W.bits, sc, W.group, len(rows), W.k, xs, xdt)
+        else:
+            yref = O.gemm_asym(p, W.bits, sc, zr, len(rows), W.k, xs, xdt)
         got = y[torch.from_numpy(ms).to(y.device)][:, torch.from_numpy(rows).to(y.device)].double().cpu().numpy()
         if xdt == "bf16":
             x64 = torch.from_numpy(xs.view(np.int16)).view(torch.bfloat16).double().numpy()
         else:
             x64 = xs.view(np.float16).astype(np.float64)
-        q = O.unpack(p, len(rows), W.k, W.bits)
-        wmax = np.abs(O.dequant(q, W.group, sc)).max(1)[None, :]
+        if zr is None:
+            wmax = np.abs(O.dequant(O.unpack(p, len(rows), W.k, W.bits), W.group, sc)).max(1)[None, :]
+        else:
+            wmax = np.abs(O.dequant_asym(O.unpack_u(p, len(rows), W.k, W.bits), sc, zr)).max(1)[None, :]
         tol = 2e-3 * np.sqrt((x64 ** 2).sum(1))[:, None] * wmax + 1e-3 * np.abs(yref)
         err = np.abs(got - yref)
         assert np.all(err <= tol), f"product {idx} (n={W.n}, k={W.k}, bits={W.bits}): " \
@@ -94,6 +102,13 @@ def test_qwen7b_decode_plan(mods):
     check_sampled(stack)
     run_step(bench, stack, "plan", order="chained")
     check_sampled(stack, seed=1)
+
+
+def test_qwen7b_decode_asym_plan(mods):
+    bench, zq = mods
+    stack = bench.Stack("qwen7b-decode-asym", None, None, torch, zq, synth)
+    run_step(bench, stack, "plan")
+    check_sampled(stack)
 
 
 def test_qwen32b_decode_plan(mods):

@@ -52,6 +52,8 @@ zq_status check_weight(const zq_weight* W) {
   if (s) return s;
   if (W->n > 0 && W->k > 0 && (!W->packed || !W->scales))
     return fail(ZQ_ERR_INVALID_ARG, "null packed or scales pointer");
+  if (W->zeros && (W->bits == 8 || W->group != 128))
+    return fail(ZQ_ERR_UNSUPPORTED, "asymmetric weights take bits 2 or 4 and group 128");
   return ZQ_OK;
 }
 
@@ -141,6 +143,7 @@ zq_status zq_pack(const void* w, zq_dtype w_dtype, int64_t n, int64_t k, int bit
   a.bits = bits;
   a.group = group;
   a.scales = scales_in ? scales_in : scales_out;
+  a.zeros = nullptr;
   a.packed = (uint8_t*)packed_out;
   a.flags = flags;
   a.stream = s;
@@ -159,14 +162,77 @@ zq_status zq_pack(const void* w, zq_dtype w_dtype, int64_t n, int64_t k, int bit
   return ok();
 }
 
+zq_status zq_pack_asym(const void* w, zq_dtype w_dtype, int64_t n, int64_t k, int bits,
+                       const uint16_t* scales_in, const uint16_t* zeros_in, void* packed_out,
+                       uint16_t* scales_out, uint16_t* zeros_out, void* stream) {
+  if (bits != 2 && bits != 4) return fail(ZQ_ERR_UNSUPPORTED, "asymmetric weights take bits 2 or 4 (bits=%d)", bits);
+  zq_status st = check_format(bits, 128, n, k);
+  if (st) return st;
+  if (w_dtype != ZQ_I8 && w_dtype != ZQ_F16 && w_dtype != ZQ_BF16 && w_dtype != ZQ_F32)
+    return fail(ZQ_ERR_INVALID_ARG, "w_dtype=%d not accepted", (int)w_dtype);
+  const bool empty = n == 0 || k == 0;
+  if (!empty && (!w || !packed_out)) return fail(ZQ_ERR_INVALID_ARG, "null w or packed_out");
+  if ((scales_in == nullptr) != (zeros_in == nullptr))
+    return fail(ZQ_ERR_INVALID_ARG, "scales_in and zeros_in go together");
+  if (w_dtype == ZQ_I8 && !scales_in && (!scales_out || !zeros_out) && !empty)
+    return fail(ZQ_ERR_INVALID_ARG, "integer codes need scales_in and zeros_in");
+  if (!scales_in && (!scales_out || !zeros_out))
+    return fail(ZQ_ERR_INVALID_ARG, "float weights need scales_in/zeros_in or scales_out/zeros_out");
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t ns = n * (k / 128);
+  hipError_t e;
+  if (scales_in && scales_out && zeros_out && ns > 0) {
+    if (scales_in != scales_out) {
+      e = hipMemcpyAsync(scales_out, scales_in, (size_t)ns * 2, hipMemcpyDeviceToDevice, s);
+      if (e != hipSuccess) return hip_fail(e, "copy scales");
+    }
+    if (zeros_in != zeros_out) {
+      e = hipMemcpyAsync(zeros_out, zeros_in, (size_t)ns * 2, hipMemcpyDeviceToDevice, s);
+      if (e != hipSuccess) return hip_fail(e, "copy zeros");
+    }
+  }
+  if (empty) {
+    e = hipStreamSynchronize(s);
+    return e == hipSuccess ? ok() : hip_fail(e, "sync");
+  }
+  uint32_t* flags = nullptr;
+  e = hipMalloc(&flags, 2 * sizeof(uint32_t));
+  if (e != hipSuccess) return hip_fail(e, "hipMalloc flags");
+  zq::PackArgs a;
+  a.w = w;
+  a.wt = (int)w_dtype;
+  a.n = n;
+  a.k = k;
+  a.bits = bits;
+  a.group = 128;
+  a.scales = scales_in ? scales_in : scales_out;
+  a.zeros = zeros_in ? zeros_in : zeros_out;
+  a.packed = (uint8_t*)packed_out;
+  a.flags = flags;
+  a.stream = s;
+  uint32_t host_flags[2] = {0, 0};
+  e = hipMemsetAsync(flags, 0, 2 * sizeof(uint32_t), s);
+  if (e == hipSuccess && w_dtype != ZQ_I8 && !scales_in) e = zq::launch_compute_scales_zeros(a, scales_out, zeros_out);
+  if (e == hipSuccess) e = zq::launch_quantize_pack_asym(a);
+  if (e == hipSuccess) e = hipMemcpyAsync(host_flags, flags, sizeof host_flags, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  hipError_t ef = hipFree(flags);
+  if (e != hipSuccess) return hip_fail(e, "pack");
+  if (ef != hipSuccess) return hip_fail(ef, "hipFree flags");
+  if (host_flags[0] & zq::FLAG_NONFINITE) return fail(ZQ_ERR_RANGE, "non-finite weight, scale or zero");
+  if (host_flags[0] & zq::FLAG_SCALE_RANGE) return fail(ZQ_ERR_RANGE, "scale or zero beyond the fp16 range");
+  if (host_flags[0] & zq::FLAG_CODE_RANGE) return fail(ZQ_ERR_RANGE, "code outside [0, %d]", (1 << bits) - 1);
+  return ok();
+}
+
 zq_status zq_unpack(const zq_weight* W, void* out, zq_dtype out_dtype, void* stream) {
   zq_status st = check_weight(W);
   if (st) return st;
   if (out_dtype != ZQ_I8 && out_dtype != ZQ_F16 && out_dtype != ZQ_BF16 && out_dtype != ZQ_F32)
     return fail(ZQ_ERR_INVALID_ARG, "out_dtype=%d not accepted", (int)out_dtype);
   if (W->n > 0 && W->k > 0 && !out) return fail(ZQ_ERR_INVALID_ARG, "null out");
-  hipError_t e = zq::launch_unpack((const uint8_t*)W->packed, W->scales, W->bits, W->group, W->n,
-                                   W->k, out, (int)out_dtype, (hipStream_t)stream);
+  hipError_t e = zq::launch_unpack((const uint8_t*)W->packed, W->scales, W->zeros, W->bits, W->group,
+                                   W->n, W->k, out, (int)out_dtype, (hipStream_t)stream);
   return e == hipSuccess ? ok() : hip_fail(e, "unpack launch");
 }
 
@@ -192,6 +258,7 @@ zq_status zq_gemm(const zq_weight* W, const void* X, zq_dtype x_dtype, int64_t m
   zq::GemmArgs a;
   a.packed = (const uint8_t*)W->packed;
   a.scales = W->scales;
+  a.zeros = W->zeros;
   a.bits = W->bits;
   a.group = W->group;
   a.n = W->n;
@@ -207,7 +274,9 @@ zq_status zq_gemm(const zq_weight* W, const void* X, zq_dtype x_dtype, int64_t m
   const int64_t rowbytes = W->k * W->bits / 8;
   const bool aligned16 = ((uintptr_t)W->packed & 15) == 0 && rowbytes % 16 == 0 &&
                          ((uintptr_t)X & 15) == 0 && (m == 1 || (ldx * 2) % 16 == 0);
-  const bool use_mstream = m >= zq::MSTREAM_MIN_M &&
+  // asymmetric weights: the vector-ALU stream kernel (m <= 4) or the general kernel
+  const bool asym = W->zeros != nullptr;
+  const bool use_mstream = !asym && m >= zq::MSTREAM_MIN_M &&
                            zq::mstream_supported(W->packed, W->scales, W->bits, W->group, m, W->k, X, ldx);
   const bool use_stream = !use_mstream && m <= 4 && aligned16 &&
                           zq::stream_supported(W->bits, W->group, m, W->n, W->k);
@@ -215,6 +284,7 @@ zq_status zq_gemm(const zq_weight* W, const void* X, zq_dtype x_dtype, int64_t m
     zq::StreamProblem p{};
     p.packed = a.packed;
     p.scales = a.scales;
+    p.zeros = a.zeros;
     p.x = a.x;
     p.y = a.y;
     p.n = a.n;
@@ -227,11 +297,11 @@ zq_status zq_gemm(const zq_weight* W, const void* X, zq_dtype x_dtype, int64_t m
     p.yt = a.yt;
     p.row_off = 0;
     e = use_stream ? zq::launch_stream_single(p, m, s) : zq::launch_mstream_single(p, m, s);
-  } else if (m <= 4 && aligned16 && zq::gemv_valu_lds_bytes(W->bits, m, W->k) <= 64 * 1024)
+  } else if (!asym && m <= 4 && aligned16 && zq::gemv_valu_lds_bytes(W->bits, m, W->k) <= 64 * 1024)
     e = zq::launch_gemv_valu(a);
-  else if (aligned16 && zq::gemm_prefill2_supported(a))
+  else if (!asym && aligned16 && zq::gemm_prefill2_supported(a))
     e = zq::launch_gemm_prefill2(a);
-  else if (aligned16 && zq::gemm_mfma_supported(a))
+  else if (!asym && aligned16 && zq::gemm_mfma_supported(a))
     e = zq::launch_gemm_mfma(a);
   else
     e = zq::launch_gemm_general(a);
@@ -286,7 +356,8 @@ zq_status zq_plan_create(const zq_problem* problems, int count, int64_t m, zq_pl
   if (mfma && m <= 4) {
     for (int i = 0; i < count && mfma; ++i) {
       const zq_problem& q = problems[i];
-      mfma = zq::mstream_supported(q.w.packed, q.w.scales, q.w.bits, q.w.group, m, q.w.k, q.x, q.ldx);
+      mfma = !q.w.zeros &&
+             zq::mstream_supported(q.w.packed, q.w.scales, q.w.bits, q.w.group, m, q.w.k, q.x, q.ldx);
     }
   }
   std::vector<zq::StreamProblem> probs(count);
@@ -307,7 +378,7 @@ zq_status zq_plan_create(const zq_problem* problems, int count, int64_t m, zq_pl
     const bool aligned = ((uintptr_t)q.w.packed & 15) == 0 && ((uintptr_t)q.x & 15) == 0 &&
                          (m == 1 || (q.ldx * 2) % 16 == 0);
     if (mfma) {
-      if (!zq::mstream_supported(q.w.packed, q.w.scales, q.w.bits, q.w.group, m, q.w.k, q.x, q.ldx))
+      if (q.w.zeros || !zq::mstream_supported(q.w.packed, q.w.scales, q.w.bits, q.w.group, m, q.w.k, q.x, q.ldx))
         return fail(ZQ_ERR_UNSUPPORTED, "problem %d: plans with m > 4 need INT4 codes, k a multiple of 512, "
                     "16-byte aligned codes and activations and 8-byte aligned scales", i);
     } else if (!aligned || !zq::stream_supported(q.w.bits, q.w.group, m, q.w.n, q.w.k)) {
@@ -320,7 +391,8 @@ zq_status zq_plan_create(const zq_problem* problems, int count, int64_t m, zq_pl
     bool new_segment = !same_phase;
     if (same_phase) {
       const zq::StreamPhase& sg = segs.back();
-      new_segment = sg.k != q.w.k || sg.bits != q.w.bits || sg.group != q.w.group || sg.xt != xt;
+      new_segment = sg.k != q.w.k || sg.bits != q.w.bits || sg.group != q.w.group || sg.xt != xt ||
+                    sg.asym != (q.w.zeros ? 1 : 0);
     }
     if (new_segment) {
       zq::StreamPhase sg{};
@@ -329,6 +401,7 @@ zq_status zq_plan_create(const zq_problem* problems, int count, int64_t m, zq_pl
       sg.bits = q.w.bits;
       sg.group = q.w.group;
       sg.xt = xt;
+      sg.asym = q.w.zeros ? 1 : 0;
       sg.wait = (i > 0 && !same_phase) ? 1 : 0;
       segs.push_back(sg);
     }
@@ -337,6 +410,7 @@ zq_status zq_plan_create(const zq_problem* problems, int count, int64_t m, zq_pl
     p = zq::StreamProblem{};
     p.packed = (const uint8_t*)q.w.packed;
     p.scales = q.w.scales;
+    p.zeros = q.w.zeros;
     p.x = (const uint16_t*)q.x;
     p.y = q.y;
     p.n = q.w.n;
@@ -394,8 +468,9 @@ zq_status zq_plan_create(const zq_problem* problems, int count, int64_t m, zq_pl
   }
   int variant = -1;
   for (const zq::StreamPhase& sg : fitted) {
-    const int v = mfma ? zq::mstream_variant_of(sg.xt, sg.group) : zq::stream_variant_of(sg.xt, sg.bits, sg.group);
-    variant = (variant == -1 || variant == v) ? v : (mfma ? 4 : 12);
+    const int v = mfma ? zq::mstream_variant_of(sg.xt, sg.group)
+                       : zq::stream_variant_of(sg.xt, sg.bits, sg.group, sg.asym);
+    variant = (variant == -1 || variant == v) ? v : (mfma ? 4 : zq::STREAM_VAR_ANY);
   }
   zq_plan_s* plan = new zq_plan_s;
   plan->nseg = (int)fitted.size();

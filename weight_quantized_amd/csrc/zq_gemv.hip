@@ -174,11 +174,12 @@ __global__ __launch_bounds__(GEMV_THREADS) void gemv_valu_kernel(
 // General kernel: one wave per output (m, row); byte-granular reads, any K
 // that the format allows, any alignment. Same arithmetic contract (fp32 sums
 // of x * q * s), different order.
+// Asymmetric weights (zeros != nullptr): unsigned codes, w = q * s + z.
 template <int XT>
 __global__ __launch_bounds__(256) void gemm_general_kernel(
     const uint8_t* __restrict__ packed, int bits, const uint16_t* __restrict__ scales,
-    int group, int64_t n, int64_t k, const uint16_t* __restrict__ x, int64_t m, int64_t ldx,
-    void* __restrict__ y, int64_t ldy, int yt) {
+    const uint16_t* __restrict__ zeros, int group, int64_t n, int64_t k, const uint16_t* __restrict__ x,
+    int64_t m, int64_t ldx, void* __restrict__ y, int64_t ldy, int yt) {
   const int lane = threadIdx.x & 63;
   const int64_t out = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (out >= m * n) return;  // whole wave leaves together
@@ -191,9 +192,11 @@ __global__ __launch_bounds__(256) void gemm_general_kernel(
     const uint32_t byte = packed[r * rowbytes + c / per];
     const int i = (int)(c % per);
     int f = (int)((byte >> (i * bits)) & ((1u << bits) - 1u));
-    if (f >= (1 << (bits - 1))) f -= (1 << bits);
-    const float s = f16_bits_to_float(group ? scales[r * G + c / group] : scales[0]);
-    acc = __builtin_fmaf(x_bits_to_float<XT>(x[mi * ldx + c]), (float)f * s, acc);
+    if (!zeros && f >= (1 << (bits - 1))) f -= (1 << bits);
+    const int64_t si = group ? r * G + c / group : 0;
+    const float s = f16_bits_to_float(scales[si]);
+    const float wv = zeros ? __builtin_fmaf((float)f, s, f16_bits_to_float(zeros[si])) : (float)f * s;
+    acc = __builtin_fmaf(x_bits_to_float<XT>(x[mi * ldx + c]), wv, acc);
   }
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) acc += __shfl_xor(acc, o, 64);
@@ -289,11 +292,11 @@ hipError_t launch_gemm_general(const GemmArgs& a) {
   const int64_t blocks = (outs + 3) / 4;
   if (a.xt == XF16)
     hipLaunchKernelGGL(gemm_general_kernel<XF16>, dim3((uint32_t)blocks), dim3(256), 0, a.stream,
-                       a.packed, a.bits, a.scales, a.group, a.n, a.k, a.x, a.m, a.ldx, a.y, a.ldy,
+                       a.packed, a.bits, a.scales, a.zeros, a.group, a.n, a.k, a.x, a.m, a.ldx, a.y, a.ldy,
                        a.yt);
   else
     hipLaunchKernelGGL(gemm_general_kernel<XBF16>, dim3((uint32_t)blocks), dim3(256), 0, a.stream,
-                       a.packed, a.bits, a.scales, a.group, a.n, a.k, a.x, a.m, a.ldx, a.y, a.ldy,
+                       a.packed, a.bits, a.scales, a.zeros, a.group, a.n, a.k, a.x, a.m, a.ldx, a.y, a.ldy,
                        a.yt);
   return hipGetLastError();
 }

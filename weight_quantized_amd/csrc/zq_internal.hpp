@@ -20,6 +20,7 @@ const DeviceInfo& device_info();
 struct GemmArgs {
   const uint8_t* packed;
   const uint16_t* scales;
+  const uint16_t* zeros = nullptr;  // asymmetric weights: fp16 zero points, [n][k/128]
   int bits, group;
   int64_t n, k;
   const uint16_t* x;
@@ -34,6 +35,7 @@ struct GemmArgs {
 // One product of the persistent decode kernel (device pointers).
 struct StreamProblem {
   const uint8_t* packed;
+  const uint16_t* zeros;  // asymmetric weights (unsigned codes): zero points, else nullptr
   const uint16_t* scales;
   const uint16_t* x;
   void* y;
@@ -48,17 +50,19 @@ struct StreamPhase {
   int32_t first, count;  // problems [first, first + count) of the problem table
   int64_t n_total, k;
   int32_t bits, group, xt, wait;
+  int32_t asym, pad;     // asym: unsigned codes with zero points
 };
 constexpr size_t STREAM_LDS_MAX = 160 * 1024;
 int stream_grid();  // workgroups of a stream launch (one per CU)
 // persistent, balanced kernel (1 <= m <= 4, rows of whole 256-byte steps)
 bool stream_supported(int bits, int group, int64_t m, int64_t n, int64_t k);
 size_t stream_lds_bytes(int bits, int64_t m, int64_t k, int nrec);
-int stream_variant_of(int xt, int bits, int group);
+int stream_variant_of(int xt, int bits, int group, int asym);
+constexpr int STREAM_VAR_ANY = 16;  // a plan mixing formats
 hipError_t launch_stream_single(const StreamProblem& p, int64_t m, hipStream_t stream);
 // dev_ranges[s * stream_grid() + w] = {first, last} product (within segment s)
 // that workgroup w touches; variant: one format code (stream_variant_of) for
-// every segment, or 12 for a mix; sync = 2 device words (counter, error)
+// every segment, or STREAM_VAR_ANY for a mix; sync = 3 device words
 hipError_t launch_stream_plan(const StreamPhase* dev_segs, int nseg, const StreamProblem* dev_probs,
                               const int2* dev_ranges, int64_t m, int variant, size_t lds, uint32_t* sync,
                               bool waits, hipStream_t stream);
@@ -97,6 +101,7 @@ struct PackArgs {
   int64_t n, k;
   int bits, group;
   const uint16_t* scales;  // scales used for quantizing (given or computed)
+  const uint16_t* zeros;   // asymmetric: zero points used for quantizing, else nullptr
   uint8_t* packed;
   uint32_t* flags;         // device: [0] error bits, [1] absmax bits
   hipStream_t stream;
@@ -104,7 +109,10 @@ struct PackArgs {
 enum : uint32_t { FLAG_NONFINITE = 1u, FLAG_SCALE_RANGE = 2u, FLAG_CODE_RANGE = 4u };
 hipError_t launch_compute_scales(const PackArgs& a, uint16_t* scales_out);
 hipError_t launch_quantize_pack(const PackArgs& a);
-hipError_t launch_unpack(const uint8_t* packed, const uint16_t* scales, int bits, int group,
-                         int64_t n, int64_t k, void* out, int out_dtype, hipStream_t stream);
+hipError_t launch_unpack(const uint8_t* packed, const uint16_t* scales, const uint16_t* zeros, int bits,
+                         int group, int64_t n, int64_t k, void* out, int out_dtype, hipStream_t stream);
+// asymmetric weights (unsigned codes, fp16 scale and zero per 128-group)
+hipError_t launch_compute_scales_zeros(const PackArgs& a, uint16_t* scales_out, uint16_t* zeros_out);
+hipError_t launch_quantize_pack_asym(const PackArgs& a);
 
 }  // namespace zq

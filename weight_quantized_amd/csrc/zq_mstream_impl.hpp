@@ -58,7 +58,7 @@ constexpr int MS_TROW = 272, MS_TLOAD = 4 * MS_TROW, MS_TTILE = 4 * MS_TLOAD;
 constexpr int MS_WSCR = MS_TW * MS_TTILE;
 
 __host__ __device__ inline size_t mstream_lds_bytes(int mt, int nrec) {
-  return (size_t)nrec * 64 + 2 * (size_t)mstream_xbuf_bytes(mt) + 8 * (size_t)MS_WSCR;
+  return (size_t)nrec * PROD_REC_BYTES + 2 * (size_t)mstream_xbuf_bytes(mt) + 8 * (size_t)MS_WSCR;
 }
 
 // INT4 decoder for the MFMA kernel: raw packed dword (codes not yet

@@ -150,10 +150,95 @@ __global__ void quantize_pack_kernel(const void* __restrict__ w, int wt, int64_t
   if (err) atomicOr(flags, err);
 }
 
+// ---------------------------------------------------------------------------
+// Asymmetric weights: the quantizer of the ZSE wiki's section on the .zse
+// model format (unsigned codes, per 128-group fp16 scale (max - min) / qmax
+// and zero point min, qmax = 2^b - 1). Codes come from the stored fp16 scale
+// and zero: q = clamp(rne((w - z) / s), 0, qmax), double arithmetic.
+
+// One thread per (row, 128-group) unit.
+__global__ void scales_zeros_kernel(const void* __restrict__ w, int wt, int64_t n, int64_t k, int bits,
+                                    uint16_t* __restrict__ scales, uint16_t* __restrict__ zeros,
+                                    uint32_t* flags) {
+  const int64_t G = k / 128;
+  const int64_t u = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (u >= n * G) return;
+  const int64_t r = u / G, g = u - r * G;
+  float lo = __builtin_inff(), hi = -__builtin_inff();
+  bool finite = true;
+  for (int i = 0; i < 128; ++i) {
+    const float v = load_w(w, wt, r * k + g * 128 + i);
+    finite = finite && __builtin_isfinite(v);
+    lo = fminf(lo, v);
+    hi = fmaxf(hi, v);
+  }
+  if (!finite) {
+    atomicOr(flags, FLAG_NONFINITE);
+    scales[u] = 0;
+    zeros[u] = 0;
+    return;
+  }
+  const double qmax = (double)((1 << bits) - 1);
+  const uint16_t s = double_to_f16_rne(((double)hi - (double)lo) / qmax);
+  const uint16_t z = double_to_f16_rne((double)lo);
+  if ((s & 0x7c00u) == 0x7c00u || (z & 0x7c00u) == 0x7c00u) atomicOr(flags, FLAG_SCALE_RANGE);
+  scales[u] = s;
+  zeros[u] = z;
+}
+
+// One thread per output byte: quantize (or range-check unsigned codes) and pack.
+__global__ void quantize_pack_asym_kernel(const void* __restrict__ w, int wt, int64_t n, int64_t k, int bits,
+                                          const uint16_t* __restrict__ scales,
+                                          const uint16_t* __restrict__ zeros, uint8_t* __restrict__ packed,
+                                          uint32_t* flags) {
+  const int per = 8 / bits;
+  const int64_t rowbytes = k / per;
+  const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (idx >= n * rowbytes) return;
+  const int64_t r = idx / rowbytes, jb = idx - r * rowbytes;
+  const int qmax = (1 << bits) - 1;
+  uint32_t byte = 0, err = 0;
+  for (int i = 0; i < per; ++i) {
+    const int64_t c = jb * per + i;
+    int q;
+    if (wt == 0) {
+      q = ((const int8_t*)w)[r * k + c];
+      if (q < 0 || q > qmax) err |= FLAG_CODE_RANGE;
+    } else {
+      const int64_t si = r * (k / 128) + c / 128;
+      const double s = f16_bits_to_double(scales[si]);
+      const double z = f16_bits_to_double(zeros[si]);
+      const double v = (double)load_w(w, wt, r * k + c);
+      if (!__builtin_isfinite(v) || !__builtin_isfinite(s) || !__builtin_isfinite(z)) err |= FLAG_NONFINITE;
+      double qd = 0.0;
+      if (s != 0.0 && __builtin_isfinite(v) && __builtin_isfinite(s) && __builtin_isfinite(z)) {
+        qd = __builtin_rint((v - z) / s);
+        qd = qd < 0.0 ? 0.0 : qd;
+        qd = qd > (double)qmax ? (double)qmax : qd;
+      }
+      q = (int)qd;
+    }
+    byte |= ((uint32_t)q & ((1u << bits) - 1u)) << (i * bits);
+  }
+  packed[idx] = (uint8_t)byte;
+  if (err) atomicOr(flags, err);
+}
+
+// double -> bfloat16 bit pattern, round to nearest even: round to odd into
+// float (24 bits, enough guard bits), then round float to bf16 (8 bits).
+__device__ uint16_t double_to_bf16_rne(double d) {
+  float f = __double2float_rz(d);
+  uint32_t b = __float_as_uint(f);
+  if ((double)f != d && __builtin_isfinite(f)) b |= 1u;  // sticky
+  return float_to_bf16_bits(__uint_as_float(b));
+}
+
 // One thread per packed byte: decode its codes into the requested output.
+// Asymmetric weights (zeros != nullptr) have unsigned codes and dequantize to
+// q * s + z, computed exactly in double and rounded once to the output type.
 __global__ void unpack_kernel(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales,
-                              int bits, int group, int64_t n, int64_t k, void* __restrict__ out,
-                              int out_dtype) {
+                              const uint16_t* __restrict__ zeros, int bits, int group, int64_t n, int64_t k,
+                              void* __restrict__ out, int out_dtype) {
   const int per = 8 / bits;
   const int64_t rowbytes = k / per;
   const int64_t idx = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -163,8 +248,20 @@ __global__ void unpack_kernel(const uint8_t* __restrict__ packed, const uint16_t
   for (int i = 0; i < per; ++i) {
     const int64_t c = jb * per + i;
     int q = (int)((byte >> (i * bits)) & ((1u << bits) - 1u));
-    if (q >= (1 << (bits - 1))) q -= (1 << bits);
     const int64_t o = r * k + c;
+    if (zeros) {
+      if (out_dtype == 0) {
+        ((int8_t*)out)[o] = (int8_t)q;
+      } else {
+        const int64_t si = r * (k / 128) + c / 128;
+        const double v = (double)q * f16_bits_to_double(scales[si]) + f16_bits_to_double(zeros[si]);
+        if (out_dtype == 3) ((float*)out)[o] = (float)v;
+        else if (out_dtype == 1) ((uint16_t*)out)[o] = double_to_f16_rne(v);
+        else ((uint16_t*)out)[o] = double_to_bf16_rne(v);
+      }
+      continue;
+    }
+    if (q >= (1 << (bits - 1))) q -= (1 << bits);
     if (out_dtype == 0) {
       ((int8_t*)out)[o] = (int8_t)q;
     } else {
@@ -201,6 +298,22 @@ hipError_t launch_compute_scales(const PackArgs& a, uint16_t* scales_out) {
   return hipGetLastError();
 }
 
+hipError_t launch_compute_scales_zeros(const PackArgs& a, uint16_t* scales_out, uint16_t* zeros_out) {
+  const int64_t units = a.n * (a.k / 128);
+  if (units > 0)
+    hipLaunchKernelGGL(scales_zeros_kernel, dim3(blocks_for(units, 256)), dim3(256), 0, a.stream, a.w, a.wt,
+                       a.n, a.k, a.bits, scales_out, zeros_out, a.flags);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_pack_asym(const PackArgs& a) {
+  const int64_t bytes = a.n * (a.k * a.bits / 8);
+  if (bytes > 0)
+    hipLaunchKernelGGL(quantize_pack_asym_kernel, dim3(blocks_for(bytes, 256)), dim3(256), 0, a.stream, a.w,
+                       a.wt, a.n, a.k, a.bits, a.scales, a.zeros, a.packed, a.flags);
+  return hipGetLastError();
+}
+
 hipError_t launch_quantize_pack(const PackArgs& a) {
   const int64_t bytes = a.n * (a.k * a.bits / 8);
   if (bytes > 0)
@@ -209,12 +322,12 @@ hipError_t launch_quantize_pack(const PackArgs& a) {
   return hipGetLastError();
 }
 
-hipError_t launch_unpack(const uint8_t* packed, const uint16_t* scales, int bits, int group,
-                         int64_t n, int64_t k, void* out, int out_dtype, hipStream_t stream) {
+hipError_t launch_unpack(const uint8_t* packed, const uint16_t* scales, const uint16_t* zeros, int bits,
+                         int group, int64_t n, int64_t k, void* out, int out_dtype, hipStream_t stream) {
   const int64_t bytes = n * (k * bits / 8);
   if (bytes > 0)
     hipLaunchKernelGGL(unpack_kernel, dim3(blocks_for(bytes, 256)), dim3(256), 0, stream, packed,
-                       scales, bits, group, n, k, out, out_dtype);
+                       scales, zeros, bits, group, n, k, out, out_dtype);
   return hipGetLastError();
 }
 

@@ -6,7 +6,8 @@ namespace zq {
 
 int stream_grid() { return device_info().num_cus; }
 
-int stream_variant_of(int xt, int bits, int group) { return stream_variant(xt, bits, group); }
+int stream_variant_of(int xt, int bits, int group, int asym) { return stream_variant(xt, bits, group, asym); }
+static_assert(VAR_ANY == STREAM_VAR_ANY, "variant numbering");
 
 size_t stream_lds_bytes(int bits, int64_t m, int64_t k, int nrec) { return stream_seg_lds(bits, m, k, nrec); }
 
@@ -44,7 +45,8 @@ hipError_t launch_stream_single(const StreamProblem& p, int64_t m, hipStream_t s
   seg.xt = p.xt;
   StreamProblem pp = p;
   pp.row_off = 0;
-  const void* fn = stream_kernel_for(m, stream_variant(p.xt, p.bits, p.group));
+  seg.asym = p.zeros ? 1 : 0;
+  const void* fn = stream_kernel_for(m, stream_variant(p.xt, p.bits, p.group, seg.asym));
   const size_t lds = stream_seg_lds(p.bits, m, p.k, 1);
   hipError_t e = ensure_lds_attr(fn, lds);
   if (e != hipSuccess) return e;

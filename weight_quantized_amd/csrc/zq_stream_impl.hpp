@@ -55,30 +55,37 @@ constexpr int st_threads() { return MR == 1 ? 1024 : 512; }
 //    by 8 serves the upper two pairs. u = q + 8. Offsets: even k 1032, odd 72.
 //  fp16 INT8: bytes in the fraction's low 8 bits: value 1024 + u, u = q + 128.
 //  everything else: the generic Decoder (one offset for all k).
-template <int XT, int BITS>
+// ASYM: unsigned codes (u = code, no sign flip), so every offset is smaller
+// by 2^(BITS-1): fp16 INT4 1024 / 64, generic 2^BITS.
+template <int XT, int BITS, bool ASYM = false>
 struct FastDec {
-  static constexpr float BE = (XT == XF16 && BITS == 4) ? 1032.f
-                              : (XT == XF16 && BITS == 8) ? 1152.f
-                                                          : Decoder<XT, BITS>::BIAS;
-  static constexpr float BO = (XT == XF16 && BITS == 4) ? 72.f : BE;
+  static constexpr float SYM_BE = (XT == XF16 && BITS == 4) ? 1032.f
+                                  : (XT == XF16 && BITS == 8) ? 1152.f
+                                                              : Decoder<XT, BITS>::BIAS;
+  static constexpr float SYM_BO = (XT == XF16 && BITS == 4) ? 72.f : SYM_BE;
+  static constexpr float BE = ASYM ? SYM_BE - (float)(1 << (BITS - 1)) : SYM_BE;
+  static constexpr float BO = ASYM ? SYM_BO - (float)(1 << (BITS - 1)) : SYM_BO;
+  static constexpr uint32_t FLIP4 = ASYM ? 0u : 0x00080008u;  // sign flip of the low-nibble pairs
+  static constexpr uint32_t FLIP4H = ASYM ? 0u : 0x00800080u;  // ... of the high-nibble pairs
+  static constexpr uint32_t FLIP8 = ASYM ? 0u : 0x00800080u;
   // dot of one raw packed dword (codes not yet sign-flipped) with its
   // activation pairs. The sign flip is folded into the masking:
   // ((v ^ S) & M) | O == (v & M) ^ ((S & M) ^ O), one v_bitop3 per pair.
   static __device__ __forceinline__ float dot(uint32_t v, const uint32_t* xq, float d) {
     if constexpr (XT == XF16 && BITS == 4) {
       const uint32_t t = v >> 8;
-      d = dot2<XF16>((v & 0x000F000Fu) ^ (0x00080008u ^ 0x64006400u), xq[0], d);
-      d = dot2<XF16>((v & 0x00F000F0u) ^ (0x00800080u ^ 0x54005400u), xq[1], d);
-      d = dot2<XF16>((t & 0x000F000Fu) ^ (0x00080008u ^ 0x64006400u), xq[2], d);
-      d = dot2<XF16>((t & 0x00F000F0u) ^ (0x00800080u ^ 0x54005400u), xq[3], d);
+      d = dot2<XF16>((v & 0x000F000Fu) ^ (FLIP4 ^ 0x64006400u), xq[0], d);
+      d = dot2<XF16>((v & 0x00F000F0u) ^ (FLIP4H ^ 0x54005400u), xq[1], d);
+      d = dot2<XF16>((t & 0x000F000Fu) ^ (FLIP4 ^ 0x64006400u), xq[2], d);
+      d = dot2<XF16>((t & 0x00F000F0u) ^ (FLIP4H ^ 0x54005400u), xq[3], d);
       return d;
     } else if constexpr (XT == XF16 && BITS == 8) {
-      d = dot2<XF16>((v & 0x00FF00FFu) ^ (0x00800080u ^ 0x64006400u), xq[0], d);
-      d = dot2<XF16>(((v >> 8) & 0x00FF00FFu) ^ (0x00800080u ^ 0x64006400u), xq[1], d);
+      d = dot2<XF16>((v & 0x00FF00FFu) ^ (FLIP8 ^ 0x64006400u), xq[0], d);
+      d = dot2<XF16>(((v >> 8) & 0x00FF00FFu) ^ (FLIP8 ^ 0x64006400u), xq[1], d);
       return d;
     } else {
       using D = Decoder<XT, BITS>;
-      v ^= Codes<BITS>::SIGNS;
+      if constexpr (!ASYM) v ^= Codes<BITS>::SIGNS;
       [&]<int... I>(std::integer_sequence<int, I...>) {
         ((d = dot2<XT>(D::template pair<I>(v), xq[I], d)), ...);
       }(std::make_integer_sequence<int, Codes<BITS>::PAIRS>{});
@@ -87,18 +94,21 @@ struct FastDec {
   }
 };
 
-// One product as the workgroup sees it (LDS record, 64 bytes).
+// One product as the workgroup sees it (LDS record, 80 bytes).
 struct ProdRec {
   const uint8_t* wbase;   // packed - roff * rowbytes: index by segment row
   const uint16_t* sbase;  // grouped: scales - roff * (k/128); per tensor: unused
+  const uint16_t* zbase;  // asymmetric: zeros - roff * (k/128); else unused
   const uint16_t* x;
   void* y;
   int64_t ldx, ldy;
   int32_t roff, pend;     // rows [roff, pend) of the segment row space
   int32_t yt;
   float tscale;           // per-tensor scale (1 when grouped)
+  int64_t pad;
 };
-static_assert(sizeof(ProdRec) == 64, "LDS record layout");
+constexpr int PROD_REC_BYTES = 80;
+static_assert(sizeof(ProdRec) == PROD_REC_BYTES, "LDS record layout");
 
 // Activation block of one 16-chunk step: for each row m, PC rows of 16
 // 16-byte pieces, then the (even, odd) sums of the step's 128-wide groups.
@@ -111,7 +121,8 @@ __host__ __device__ inline size_t stream_block_bytes(int bits, int64_t mr) {
 __host__ __device__ inline size_t stream_seg_lds(int bits, int64_t mr, int64_t k, int nrec) {
   const int64_t C = k / (128 / bits);
   const int nw = mr == 1 ? 16 : 8;  // waves
-  return (size_t)nrec * 64 + (size_t)nrec * (C / 16) * stream_block_bytes(bits, mr) + (size_t)nw * (8 + 32 * mr);
+  return (size_t)nrec * PROD_REC_BYTES + (size_t)nrec * (C / 16) * stream_block_bytes(bits, mr) +
+         (size_t)nw * (8 + 32 * mr);
 }
 
 // 16 bytes of activations, optionally with agent-coherent loads (the buffer
@@ -148,6 +159,7 @@ __device__ __forceinline__ ProdRec make_rec(const StreamProblem& p, int64_t rowb
   ProdRec r;
   r.wbase = p.packed - p.row_off * rowbytes;
   r.sbase = p.scales - (grouped ? p.row_off * GS : 0);
+  r.zbase = p.zeros ? p.zeros - p.row_off * GS : nullptr;
   r.x = p.x;
   r.y = p.y;
   r.ldx = p.ldx;
@@ -174,12 +186,13 @@ __device__ __forceinline__ int rec_of(const ProdRec* rec, int nrec, int32_t row)
 // bytes). Each wave takes an equal, contiguous run of quad-steps (quad-major),
 // its 16-lane group q4 handling row 4*quad + q4, so all four groups of a wave
 // cross row ends together: every branch of the main loop is wave-uniform.
-template <int XT, int BITS, bool GROUPED, int MR>
+template <int XT, int BITS, bool GROUPED, int MR, bool ASYM = false>
 __device__ __forceinline__ void run_segment(const StreamPhase& seg, const StreamProblem* probs,
                                             const StreamProblem& single, int2 wr, uint8_t* smem,
                                             uint32_t* sync, uint32_t wait_target, bool coherent) {
   using CD = Codes<BITS>;
-  using FD = FastDec<XT, BITS>;
+  using FD = FastDec<XT, BITS, ASYM>;
+  static_assert(!ASYM || GROUPED, "zero points come per 128-group");
   constexpr int NT = st_threads<MR>();
   constexpr int NW = NT / 64;      // waves
   constexpr int WPC = 128 / BITS;  // weights per 16-byte chunk
@@ -259,10 +272,16 @@ __device__ __forceinline__ void run_segment(const StreamPhase& seg, const Stream
   int lpi = rec_at(lrow);
   const u4* lptr = reinterpret_cast<const u4*>(rec[lpi].wbase + (int64_t)lrow * rowbytes) + lb * 16 + j;
   const uint16_t* lsp = GROUPED ? rec[lpi].sbase + (int64_t)lrow * GS + lb * SPS + j / CPG : nullptr;
+  // zero points sit at the same index in their own [n][k/128] array
+  auto zdiff = [&](int pi_) __attribute__((always_inline)) -> int64_t {
+    return ((int64_t)(uintptr_t)rec[pi_].zbase - (int64_t)(uintptr_t)rec[pi_].sbase) / 2;
+  };
+  int64_t zoff = ASYM ? zdiff(lpi) : 0;
   int32_t lleft = (int32_t)(s1 - s0);  // quad-steps not yet requested
-  auto next_chunk = [&](u4& wvv, uint16_t& sv) __attribute__((always_inline)) {
+  auto next_chunk = [&](u4& wvv, uint16_t& sv, uint16_t& zv) __attribute__((always_inline)) {
     wvv = __builtin_nontemporal_load(to_global(lptr));
     if constexpr (GROUPED) sv = *to_global(lsp);
+    if constexpr (ASYM) zv = *to_global(lsp + zoff);
     if (lleft > 1) {  // wave-uniform
       --lleft;
       if (++lb == CB) {
@@ -272,6 +291,7 @@ __device__ __forceinline__ void run_segment(const StreamPhase& seg, const Stream
         while (lrow >= rec[lpi].pend) ++lpi;
         lptr = reinterpret_cast<const u4*>(rec[lpi].wbase + (int64_t)lrow * rowbytes) + j;
         if constexpr (GROUPED) lsp = rec[lpi].sbase + (int64_t)lrow * GS + j / CPG;
+        if constexpr (ASYM) zoff = zdiff(lpi);
       } else {
         lptr += 16;
         if constexpr (GROUPED) lsp += SPS;
@@ -378,10 +398,10 @@ __device__ __forceinline__ void run_segment(const StreamPhase& seg, const Stream
   // go out before most of the weights, so they are not queued behind them
   constexpr int U0 = 2;
   u4 buf[U];
-  uint16_t sbuf[U];
+  uint16_t sbuf[U], zbuf[U];
   if (!sync) load_x_round(0);
 #pragma unroll
-  for (int u = 0; u < U0; ++u) next_chunk(buf[u], sbuf[u]);
+  for (int u = 0; u < U0; ++u) next_chunk(buf[u], sbuf[u], zbuf[u]);
   if (sync) {
     // weights and scales do not depend on earlier phases: already in flight
     if (tid == 0) {
@@ -399,7 +419,7 @@ __device__ __forceinline__ void run_segment(const StreamPhase& seg, const Stream
   }
   store_x_round(0);
 #pragma unroll
-  for (int u = U0; u < U; ++u) next_chunk(buf[u], sbuf[u]);
+  for (int u = U0; u < U; ++u) next_chunk(buf[u], sbuf[u], zbuf[u]);
   for (int64_t it0 = XR; it0 * NT < P; it0 += XR) {
     load_x_round(it0);
     store_x_round(it0);
@@ -427,10 +447,13 @@ __device__ __forceinline__ void run_segment(const StreamPhase& seg, const Stream
     for (int u = 0; u < U; ++u) {
       const u4 wq = buf[u];
       const uint16_t sv = sbuf[u];
-      next_chunk(buf[u], sbuf[u]);  // the chunk U steps ahead (or the stand-in)
+      const uint16_t zv = zbuf[u];
+      next_chunk(buf[u], sbuf[u], zbuf[u]);  // the chunk U steps ahead (or the stand-in)
       if (s0 + sb + u < s1) {       // wave-uniform
-        float sc = 1.f;
+        float sc = 1.f, zs = 0.f;
         if constexpr (GROUPED) sc = f16_bits_to_float(sv);
+        // zero point term z * (sum of the group's x), added by the group's first lane
+        if constexpr (ASYM) zs = gfirst ? f16_bits_to_float(zv) : 0.f;
 #pragma unroll
         for (int m = 0; m < MR; ++m) {
           // activation pairs of dword dw are pairs [dw*PAIRS, (dw+1)*PAIRS) of
@@ -455,6 +478,7 @@ __device__ __forceinline__ void run_segment(const StreamPhase& seg, const Stream
           const float part = d - fe * xsm[0] - fo * xsm[1];
           if constexpr (GROUPED) acc[m] = __builtin_fmaf(sc, part, acc[m]);
           else acc[m] += part;
+          if constexpr (ASYM) acc[m] = __builtin_fmaf(zs, xsm[0] + xsm[1], acc[m]);
         }
         xp8 += BS;
         if (++cb == CB) {  // wave-uniform: the four rows of this quad end
@@ -526,20 +550,28 @@ __device__ __forceinline__ void run_segment(const StreamPhase& seg, const Stream
   __syncthreads();  // LDS is reused by the next segment
 }
 
-// variant = (x fp16 ? 0 : 6) + (bits 2/4/8 -> 0/2/4) + (grouped ? 1 : 0)
-__host__ __device__ inline int stream_variant(int xt, int bits, int group) {
+// variant = (x fp16 ? 0 : 6) + (bits 2/4/8 -> 0/2/4) + (grouped ? 1 : 0);
+// asymmetric (grouped, bits 2/4): 12 + (x fp16 ? 0 : 2) + (bits 4 ? 1 : 0)
+__host__ __device__ inline int stream_variant(int xt, int bits, int group, int asym) {
+  if (asym) return 12 + (xt == XF16 ? 0 : 2) + (bits == 4 ? 1 : 0);
   return (xt == XF16 ? 0 : 6) + (bits == 2 ? 0 : bits == 4 ? 2 : 4) + (group ? 1 : 0);
 }
-constexpr int VAR_ANY = 12;
+constexpr int VAR_ANY = 16;
 
 template <int MR, int V>
 __device__ __forceinline__ void run_variant(const StreamPhase& seg, const StreamProblem* probs,
                                             const StreamProblem& single, int2 wr, uint8_t* smem,
                                             uint32_t* sync, uint32_t wt, bool coh) {
-  constexpr int XT = V < 6 ? XF16 : XBF16;
-  constexpr int BITS = (V % 6) / 2 == 0 ? 2 : (V % 6) / 2 == 1 ? 4 : 8;
-  constexpr bool GROUPED = (V % 2) == 1;
-  run_segment<XT, BITS, GROUPED, MR>(seg, probs, single, wr, smem, sync, wt, coh);
+  if constexpr (V >= 12) {
+    constexpr int XT = V < 14 ? XF16 : XBF16;
+    constexpr int BITS = (V & 1) ? 4 : 2;
+    run_segment<XT, BITS, true, MR, true>(seg, probs, single, wr, smem, sync, wt, coh);
+  } else {
+    constexpr int XT = V < 6 ? XF16 : XBF16;
+    constexpr int BITS = (V % 6) / 2 == 0 ? 2 : (V % 6) / 2 == 1 ? 4 : 8;
+    constexpr bool GROUPED = (V % 2) == 1;
+    run_segment<XT, BITS, GROUPED, MR>(seg, probs, single, wr, smem, sync, wt, coh);
+  }
 }
 
 template <int MR, int VAR>
@@ -549,7 +581,7 @@ __device__ __forceinline__ void seg_dispatch(const StreamPhase& seg, const Strea
   if constexpr (VAR != VAR_ANY) {
     run_variant<MR, VAR>(seg, probs, single, wr, smem, sync, wt, coh);
   } else {
-    switch (stream_variant(seg.xt, seg.bits, seg.group)) {
+    switch (stream_variant(seg.xt, seg.bits, seg.group, seg.asym)) {
       case 0: run_variant<MR, 0>(seg, probs, single, wr, smem, sync, wt, coh); break;
       case 1: run_variant<MR, 1>(seg, probs, single, wr, smem, sync, wt, coh); break;
       case 2: run_variant<MR, 2>(seg, probs, single, wr, smem, sync, wt, coh); break;
@@ -561,7 +593,11 @@ __device__ __forceinline__ void seg_dispatch(const StreamPhase& seg, const Strea
       case 8: run_variant<MR, 8>(seg, probs, single, wr, smem, sync, wt, coh); break;
       case 9: run_variant<MR, 9>(seg, probs, single, wr, smem, sync, wt, coh); break;
       case 10: run_variant<MR, 10>(seg, probs, single, wr, smem, sync, wt, coh); break;
-      default: run_variant<MR, 11>(seg, probs, single, wr, smem, sync, wt, coh); break;
+      case 11: run_variant<MR, 11>(seg, probs, single, wr, smem, sync, wt, coh); break;
+      case 12: run_variant<MR, 12>(seg, probs, single, wr, smem, sync, wt, coh); break;
+      case 13: run_variant<MR, 13>(seg, probs, single, wr, smem, sync, wt, coh); break;
+      case 14: run_variant<MR, 14>(seg, probs, single, wr, smem, sync, wt, coh); break;
+      default: run_variant<MR, 15>(seg, probs, single, wr, smem, sync, wt, coh); break;
     }
   }
 }
@@ -633,6 +669,10 @@ static const void* stream_fn_var(int var) {
     case 9: return stream_fn<MR, 9>();
     case 10: return stream_fn<MR, 10>();
     case 11: return stream_fn<MR, 11>();
+    case 12: return stream_fn<MR, 12>();
+    case 13: return stream_fn<MR, 13>();
+    case 14: return stream_fn<MR, 14>();
+    case 15: return stream_fn<MR, 15>();
     default: return stream_fn<MR, VAR_ANY>();
   }
 }

@@ -95,3 +95,12 @@ def device_scales_abs_normal(count: int, seed: int, device):
     gen.manual_seed(seed)
     v = torch.randn(count, dtype=torch.float32, device=device, generator=gen)
     return (v.abs() * 0.01 + 1e-3).to(torch.float16)
+
+
+def device_zeros_normal(count: int, seed: int, device):
+    """float16 N(0,1) * 0.01 zero points (asymmetric weights) drawn on `device`."""
+    import torch
+    gen = torch.Generator(device=device)
+    gen.manual_seed(seed)
+    v = torch.randn(count, generator=gen, device=device, dtype=torch.float32) * 0.01
+    return v.to(torch.float16)

@@ -20,7 +20,7 @@ I8, F16, BF16, F32 = 0, 1, 2, 3
 _DT = {torch.int8: I8, torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
 
 # every exported symbol of include/zq.h
-SYMBOLS = ("zq_packed_bytes", "zq_num_scales", "zq_pack", "zq_unpack", "zq_gemv", "zq_gemm",
+SYMBOLS = ("zq_packed_bytes", "zq_num_scales", "zq_pack", "zq_pack_asym", "zq_unpack", "zq_gemv", "zq_gemm",
            "zq_plan_create", "zq_plan_run", "zq_plan_check", "zq_plan_destroy",
            "zq_status_string", "zq_last_error")
 
@@ -33,7 +33,8 @@ class ZqError(RuntimeError):
 
 class _Weight(ctypes.Structure):
     _fields_ = [("bits", ctypes.c_int32), ("group", ctypes.c_int32), ("n", ctypes.c_int64),
-                ("k", ctypes.c_int64), ("packed", ctypes.c_void_p), ("scales", ctypes.c_void_p)]
+                ("k", ctypes.c_int64), ("packed", ctypes.c_void_p), ("scales", ctypes.c_void_p),
+                ("zeros", ctypes.c_void_p)]
 
 
 class _Problem(ctypes.Structure):
@@ -59,10 +60,11 @@ def lib() -> ctypes.CDLL:
         L.zq_num_scales.argtypes = [i32, i64, i64]
         L.zq_num_scales.restype = i64
         L.zq_pack.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp, vp, vp]
+        L.zq_pack_asym.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp, vp, vp, vp]
         L.zq_unpack.argtypes = [wp, vp, i32, vp]
         L.zq_gemv.argtypes = [wp, vp, i32, vp, i32, vp]
         L.zq_gemm.argtypes = [wp, vp, i32, i64, i64, vp, i32, i64, vp]
-        for f in ("zq_pack", "zq_unpack", "zq_gemv", "zq_gemm"):
+        for f in ("zq_pack", "zq_pack_asym", "zq_unpack", "zq_gemv", "zq_gemm"):
             getattr(L, f).restype = i32
         L.zq_plan_create.argtypes = [ctypes.POINTER(_Problem), i32, i64, ctypes.POINTER(vp)]
         L.zq_plan_run.argtypes = [vp, vp]
@@ -101,20 +103,24 @@ def num_scales(group: int, n: int, k: int) -> int:
 
 @dataclass
 class ZqWeight:
-    """A packed weight matrix in device memory: codes [n][k*bits/8] uint8 and fp16 scales."""
+    """A packed weight matrix in device memory: codes [n][k*bits/8] uint8 and
+    fp16 scales; with `zeros` (fp16 [n][k/128]) the codes are unsigned and the
+    weights asymmetric (w = q * s + z)."""
     bits: int
     group: int
     n: int
     k: int
     packed: torch.Tensor
     scales: torch.Tensor
+    zeros: torch.Tensor | None = None
 
     def desc(self) -> _Weight:
-        return _Weight(self.bits, self.group, self.n, self.k, _ptr(self.packed), _ptr(self.scales))
+        return _Weight(self.bits, self.group, self.n, self.k, _ptr(self.packed), _ptr(self.scales),
+                       _ptr(self.zeros))
 
     @property
     def nbytes(self) -> int:
-        return self.packed.numel() + 2 * self.scales.numel()
+        return self.packed.numel() + 2 * self.scales.numel() + (0 if self.zeros is None else 2 * self.zeros.numel())
 
 
 def pack(w: torch.Tensor, bits: int, group: int, scales: torch.Tensor | None = None) -> ZqWeight:
@@ -129,6 +135,23 @@ def pack(w: torch.Tensor, bits: int, group: int, scales: torch.Tensor | None = N
     _check(lib().zq_pack(_ptr(w), _DT.get(w.dtype, -1), n, k, bits, group, _ptr(sin), _ptr(packed),
                          _ptr(out_scales), _stream(w)), "zq_pack")
     return ZqWeight(bits, group, n, k, packed, out_scales)
+
+
+def pack_asym(w: torch.Tensor, bits: int, scales: torch.Tensor | None = None,
+              zeros: torch.Tensor | None = None) -> ZqWeight:
+    """Asymmetric quantize (float w) or bit-pack (int8 unsigned codes) an [n][k]
+    device tensor, with fp16 scale and zero point per 128-group. Synchronous."""
+    n, k = w.shape
+    w = w.contiguous()
+    packed = torch.empty(max(packed_bytes(bits, n, k), 0), dtype=torch.uint8, device=w.device)
+    ng = max(n * (k // 128), 1)
+    out_s = torch.empty(ng, dtype=torch.float16, device=w.device)
+    out_z = torch.empty(ng, dtype=torch.float16, device=w.device)
+    sin = None if scales is None else scales.contiguous()
+    zin = None if zeros is None else zeros.contiguous()
+    _check(lib().zq_pack_asym(_ptr(w), _DT.get(w.dtype, -1), n, k, bits, _ptr(sin), _ptr(zin), _ptr(packed),
+                              _ptr(out_s), _ptr(out_z), _stream(w)), "zq_pack_asym")
+    return ZqWeight(bits, 128, n, k, packed, out_s, out_z)
 
 
 def unpack(W: ZqWeight, dtype: torch.dtype = torch.int8) -> torch.Tensor:
