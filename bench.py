@@ -16,6 +16,9 @@ Prints one JSON line. Other workloads (--config):
   qwen32b-decode       64 layers of Qwen2.5-32B projection shapes, M = 1
   qwen7b-decode-asym   the 7B decode stack with asymmetric INT4 weights (unsigned
                        codes, fp16 scale and zero point per 128-group)
+  qwen7b-decode-tp4    one rank's shard of the 7B decode stack under 4-way tensor
+                       parallelism (q/k/v/gate/up split by rows, o/down by
+                       columns: K = 896 and 4736 rows end in a partial step)
   qwen7b-prefill       7B stack, bits per layer from {2,4,8}, per-tensor scales,
                        M = 2048 bf16 tokens (MFMA-bound: TFLOP/s)
   hbm-copy             a plain 1 GiB device-to-device copy (torch), the
@@ -67,7 +70,7 @@ def parse():
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", default="qwen7b-decode",
                    choices=["gemv-512", "qwen7b-decode", "qwen7b-batch", "qwen32b-decode", "qwen7b-prefill",
-                            "qwen7b-decode-asym", "hbm-copy"])
+                            "qwen7b-decode-asym", "qwen7b-decode-tp4", "hbm-copy"])
     p.add_argument("--m", type=int, default=None, help="activation rows (qwen7b-batch)")
     p.add_argument("--launch", default=None, choices=["plan", "graph", "eager"],
                    help="plan: one resident launch per step (m <= 32, the default there); "
@@ -95,6 +98,8 @@ class Stack:
             shapes, L, bits_of, group, xdt, self.m = [("w", 512, 512)], 1, (lambda l: 4), 0, "f16", 1
         elif cfg in ("qwen7b-decode", "qwen7b-decode-asym"):
             shapes, L, bits_of, group, xdt, self.m = synth.QWEN25_7B, 28, (lambda l: 4), 128, "f16", 1
+        elif cfg == "qwen7b-decode-tp4":
+            shapes, L, bits_of, group, xdt, self.m = synth.QWEN25_7B_TP4, 28, (lambda l: 4), 128, "f16", 1
         elif cfg == "qwen7b-batch":
             shapes, L, bits_of, group, xdt, self.m = synth.QWEN25_7B, 28, (lambda l: 4), 128, "bf16", m or 8
         elif cfg == "qwen32b-decode":
@@ -282,8 +287,7 @@ def copy_bench(a, torch):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(f"bench.py: this build runs on one GPU only; --gpus {a.gpus} is not supported "
-              "(the sharded path is described in DESIGN.md)", file=sys.stderr)
+        print(f"bench.py measures one GPU; --gpus {a.gpus} is not supported", file=sys.stderr)
         sys.exit(2)
     import torch
     from weight_quantized_amd import synth, zq
@@ -389,6 +393,8 @@ def main():
         "qwen7b-decode": "Qwen2.5-7B-shaped decode stack: 28 layers x 7 projections, M=1, INT4 group-128, fp16 x",
         "qwen7b-decode-asym": "Qwen2.5-7B-shaped decode stack: 28 layers x 7 projections, M=1, asymmetric INT4 "
                               "(fp16 scale and zero point per 128-group), fp16 x",
+        "qwen7b-decode-tp4": "one rank's 4-way tensor-parallel shard of the Qwen2.5-7B decode stack: 28 layers "
+                             "x 7 projections, M=1, INT4 group-128, fp16 x",
         "qwen7b-batch": f"Qwen2.5-7B-shaped stack, M={stack.m}, INT4 group-128, bf16 x",
         "qwen32b-decode": "Qwen2.5-32B-shaped decode stack: 64 layers x 7 projections, M=1, INT4 group-128, fp16 x",
         "qwen7b-prefill": "Qwen2.5-7B-shaped prefill stack, per-layer INT2/INT4/INT8, per-tensor scale, M=2048, bf16 x",

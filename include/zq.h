@@ -199,8 +199,9 @@ zq_status zq_gemv(const zq_weight* W, const void* x, zq_dtype x_dtype, void* y,
  * Kernels by shape (all give results within the same tolerance of the exact
  * sums; integer-valued inputs give exact sums on every path). Asymmetric
  * weights run on the m <= 4 vector-ALU kernel or the general kernel:
- *   m = 1 (and m <= 4 for INT2/INT8): a vector-ALU kernel that streams the
- *     codes once with 128-bit loads;
+ *   m = 1, k a multiple of 128 (m <= 4 where the MFMA kernel below does
+ *     not apply): a vector-ALU kernel that streams the codes once with
+ *     128-bit loads;
  *   m = 2..32, INT4, k a multiple of 512, 16-byte aligned codes and
  *     activations, 8-byte aligned scales: a resident MFMA kernel that streams
  *     the codes once;
@@ -228,16 +229,17 @@ zq_status zq_gemm(const zq_weight* W, const void* X, zq_dtype x_dtype, int64_t m
  *              stored their outputs, so Y of one phase may be X of the next
  *              (q,k,v -> o -> gate,up -> down of a decoder layer). Problems of
  *              one phase are independent and must not write what another one
- *              of that phase reads. Consecutive problems of a phase that share
- *              k, bits, group and x dtype are streamed as one row space (any
- *              number of them), split evenly over the workgroups.
+ *              of that phase reads. The problems of a phase that share k,
+ *              bits, group, zero points (present or not) and x dtype are
+ *              streamed as one row space (any number of them, wherever they
+ *              sit in the phase), split evenly over the workgroups.
  * zq_plan_create  validates every problem (as zq_gemm does) and requires
  *              1 <= m <= 32 (ZQ_ERR_UNSUPPORTED otherwise). For m >= 2, when
  *              every problem is INT4 with k a multiple of 512, 16-byte aligned
  *              codes and activations and 8-byte aligned scales, the plan runs
  *              on the MFMA kernel; otherwise (m <= 4 only) on the vector-ALU
- *              kernel, which needs packed rows whose byte length is a multiple
- *              of 256, 16-byte aligned pointers and activations of one problem
+ *              kernel, which needs k a multiple of 128, 16-byte aligned
+ *              pointers and activations of one problem
  *              that fit in the 160 KiB of LDS with their group sums (m * k * 2
  *              bytes plus 1/32 of that). The plan
  *              copies the list to device memory and allocates three device

@@ -4,6 +4,7 @@ and activation rows are copied back and recomputed by the fp64 oracle.
 
     Qwen2.5-7B decode stack   (28 layers x 7, M = 1, INT4 g128, fp16 x), plan
     Qwen2.5-7B decode stack with asymmetric INT4 weights, plan
+    one rank's share of the 7B decode stack under 4-way tensor parallelism, plan
     Qwen2.5-32B decode stack  (64 layers x 7, M = 1), plan
     7B stack, M = 8 and 32 (bf16 x), plan (MFMA batched-decode kernel)
     7B prefill stack (per-layer INT2/4/8, per-tensor scale, M = 2048, bf16 x),
@@ -109,6 +110,16 @@ def test_qwen7b_decode_asym_plan(mods):
     stack = bench.Stack("qwen7b-decode-asym", None, None, torch, zq, synth)
     run_step(bench, stack, "plan")
     check_sampled(stack)
+
+
+def test_qwen7b_tp4_shard_decode_plan(mods):
+    # o and down rows (K = 896, 4736) end in a partial step of the decode kernel
+    bench, zq = mods
+    stack = bench.Stack("qwen7b-decode-tp4", None, None, torch, zq, synth)
+    run_step(bench, stack, "plan")
+    check_sampled(stack)
+    run_step(bench, stack, "plan", order="chained")
+    check_sampled(stack, seed=2)
 
 
 def test_qwen32b_decode_plan(mods):

@@ -129,8 +129,8 @@ def test_plan_many_phases_on_one_stream_with_other_work():
 
 
 def test_plan_validation():
-    _, _, _, Wbad = weight(4, 128, 64, 384, seed=1)      # 192-byte rows: not a multiple of 256
-    X = torch.zeros((1, 384), dtype=torch.float16, device=DEV)
+    _, _, _, Wbad = weight(4, 0, 64, 320, seed=1)        # k = 320: not whole 128-groups
+    X = torch.zeros((1, 320), dtype=torch.float16, device=DEV)
     with pytest.raises(zq.ZqError) as e:
         zq.Plan([(Wbad, X, torch.empty((1, 64), device=DEV), 0)])
     assert e.value.status == zq.ERR_UNSUPPORTED

@@ -7,6 +7,7 @@
 
 #include <algorithm>
 #include <mutex>
+#include <tuple>
 #include <vector>
 
 #include "zq.h"
@@ -382,12 +383,31 @@ zq_status zq_plan_create(const zq_problem* problems, int count, int64_t m, zq_pl
         return fail(ZQ_ERR_UNSUPPORTED, "problem %d: plans with m > 4 need INT4 codes, k a multiple of 512, "
                     "16-byte aligned codes and activations and 8-byte aligned scales", i);
     } else if (!aligned || !zq::stream_supported(q.w.bits, q.w.group, m, q.w.n, q.w.k)) {
-      return fail(ZQ_ERR_UNSUPPORTED, "problem %d: needs 16-byte alignment, rows of 256-byte multiples "
+      return fail(ZQ_ERR_UNSUPPORTED, "problem %d: needs 16-byte alignment, k a multiple of 128 "
                   "and activations that fit in LDS", i);
     }
+  }
+  // Products of one phase do not depend on each other: order them by format
+  // (activation type, bit width, scale group, zero points, k), stably, so
+  // that each format of a phase is one segment. Few large segments keep every
+  // workgroup's load pipeline full; a segment boundary drains it.
+  std::vector<int> order(count);
+  for (int i = 0; i < count; ++i) order[i] = i;
+  auto fmt_key = [&](int i) {
+    const zq_problem& q = problems[i];
+    return std::make_tuple(q.x_dtype, q.w.bits, q.w.group, q.w.zeros ? 1 : 0, q.w.k);
+  };
+  for (int a = 0; a < count;) {
+    int b = a + 1;
+    while (b < count && problems[b].phase == problems[a].phase) ++b;
+    std::stable_sort(order.begin() + a, order.begin() + b, [&](int u, int v) { return fmt_key(u) < fmt_key(v); });
+    a = b;
+  }
+  for (int i = 0; i < count; ++i) {
+    const zq_problem& q = problems[order[i]];
     const int xt = q.x_dtype == ZQ_F16 ? zq::XF16 : zq::XBF16;
     // a new segment when the phase or the format changes
-    const bool same_phase = i > 0 && q.phase == problems[i - 1].phase;
+    const bool same_phase = i > 0 && q.phase == problems[order[i - 1]].phase;
     bool new_segment = !same_phase;
     if (same_phase) {
       const zq::StreamPhase& sg = segs.back();
@@ -450,7 +470,7 @@ zq_status zq_plan_create(const zq_problem* problems, int count, int64_t m, zq_pl
       const size_t need = mfma ? zq::mstream_lds(m, maxrec) : zq::stream_lds_bytes(sg.bits, m, sg.k, maxrec);
       if (need > zq::STREAM_LDS_MAX) {
         if (sg.count == 1)
-          return fail(ZQ_ERR_UNSUPPORTED, "problem %d needs %zu bytes of LDS (max %zu)", sg.first, need,
+          return fail(ZQ_ERR_UNSUPPORTED, "problem %d needs %zu bytes of LDS (max %zu)", order[sg.first], need,
                       zq::STREAM_LDS_MAX);
         zq::StreamPhase a = sg, b = sg;
         a.count = sg.count / 2;

@@ -14,9 +14,7 @@ size_t stream_lds_bytes(int bits, int64_t m, int64_t k, int nrec) { return strea
 bool stream_supported(int bits, int group, int64_t m, int64_t n, int64_t k) {
   (void)group;
   (void)n;
-  const int64_t wpc = 128 / bits;
-  if (m < 1 || m > 4 || k % wpc != 0 || k == 0) return false;
-  if ((k / wpc) % 16 != 0) return false;  // whole 256-byte steps per row
+  if (m < 1 || m > 4 || k % 128 != 0 || k == 0) return false;  // whole 128-groups; a row's last step may be partial
   return stream_seg_lds(bits, m, k, 1) <= STREAM_LDS_MAX;
 }
 

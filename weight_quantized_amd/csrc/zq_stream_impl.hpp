@@ -121,7 +121,7 @@ __host__ __device__ inline size_t stream_block_bytes(int bits, int64_t mr) {
 __host__ __device__ inline size_t stream_seg_lds(int bits, int64_t mr, int64_t k, int nrec) {
   const int64_t C = k / (128 / bits);
   const int nw = mr == 1 ? 16 : 8;  // waves
-  return (size_t)nrec * PROD_REC_BYTES + (size_t)nrec * (C / 16) * stream_block_bytes(bits, mr) +
+  return (size_t)nrec * PROD_REC_BYTES + (size_t)nrec * ((C + 15) / 16) * stream_block_bytes(bits, mr) +
          (size_t)nw * (8 + 32 * mr);
 }
 
@@ -211,7 +211,9 @@ __device__ __forceinline__ void run_segment(const StreamPhase& seg, const Stream
   const int G = gridDim.x;
   const int64_t N = seg.n_total, k = seg.k;
   const int32_t C = (int32_t)(k / WPC);
-  const int32_t CB = C / 16;  // column blocks (steps) per row
+  const int32_t CB = (C + 15) / 16;     // column blocks (steps) per row
+  const int32_t CT = C - (CB - 1) * 16;  // chunks in a row's last step (1..16)
+  const int32_t CP = CB * 16;            // chunks per row with the last step padded
   const int64_t rowbytes = (int64_t)C * 16;
   const int32_t GS = (int32_t)(k / 128);
   const int64_t w = blockIdx.x;
@@ -265,13 +267,22 @@ __device__ __forceinline__ void run_segment(const StreamPhase& seg, const Stream
   // Within a quad row the lane's pointers advance by one step (256 bytes,
   // 16/CPG scales); at a block wrap they move to the lane's row of the next
   // quad. At the end of its run a wave keeps re-reading its last chunks
-  // (cached); the consumer discards those.
+  // (cached); the consumer discards those. When a row's last step is partial
+  // (C % 16 != 0), its lanes past the row's end re-read the row's last chunk
+  // (and its group's scale): their activations are staged as zeros.
+  const int32_t tdel = j >= CT ? CT - 1 - j : 0;                // u4 units
+  const int32_t sdel = j >= CT ? (CT - 1) / CPG - j / CPG : 0;  // scale units
+  const int64_t tdel_b = (int64_t)tdel * 16, sdel_b = (int64_t)sdel * 2;  // bytes
+  const bool ragged = CT != 16;
   int32_t lq = (int32_t)(s0 / CB), lb = (int32_t)(s0 % CB);
   if (s1 == s0) { lq = 0; lb = 0; }  // empty run: a valid stand-in address
   int32_t lrow = quad_row(lq);
   int lpi = rec_at(lrow);
-  const u4* lptr = reinterpret_cast<const u4*>(rec[lpi].wbase + (int64_t)lrow * rowbytes) + lb * 16 + j;
-  const uint16_t* lsp = GROUPED ? rec[lpi].sbase + (int64_t)lrow * GS + lb * SPS + j / CPG : nullptr;
+  const bool last0 = lb == CB - 1;
+  const u4* lptr =
+      reinterpret_cast<const u4*>(rec[lpi].wbase + (int64_t)lrow * rowbytes) + lb * 16 + j + (last0 ? tdel : 0);
+  const uint16_t* lsp =
+      GROUPED ? rec[lpi].sbase + (int64_t)lrow * GS + lb * SPS + j / CPG + (last0 ? sdel : 0) : nullptr;
   // zero points sit at the same index in their own [n][k/128] array
   auto zdiff = [&](int pi_) __attribute__((always_inline)) -> int64_t {
     return ((int64_t)(uintptr_t)rec[pi_].zbase - (int64_t)(uintptr_t)rec[pi_].sbase) / 2;
@@ -289,27 +300,36 @@ __device__ __forceinline__ void run_segment(const StreamPhase& seg, const Stream
         ++lq;
         lrow = quad_row(lq);
         while (lrow >= rec[lpi].pend) ++lpi;
-        lptr = reinterpret_cast<const u4*>(rec[lpi].wbase + (int64_t)lrow * rowbytes) + j;
-        if constexpr (GROUPED) lsp = rec[lpi].sbase + (int64_t)lrow * GS + j / CPG;
+        lptr = reinterpret_cast<const u4*>(rec[lpi].wbase + (int64_t)lrow * rowbytes) + j + (CB == 1 ? tdel : 0);
+        if constexpr (GROUPED) lsp = rec[lpi].sbase + (int64_t)lrow * GS + j / CPG + (CB == 1 ? sdel : 0);
         if constexpr (ASYM) zoff = zdiff(lpi);
       } else {
         lptr += 16;
         if constexpr (GROUPED) lsp += SPS;
+        if (ragged && lb == CB - 1) {  // wave-uniform: the row's partial last step
+          // an empty volatile asm keeps this a scalar branch: folded into
+          // per-step selects, the rare adjustment costs six VALU ops a step
+          __asm__ volatile("");
+          lptr = reinterpret_cast<const u4*>(reinterpret_cast<const uint8_t*>(lptr) + tdel_b);
+          if constexpr (GROUPED)
+            lsp = reinterpret_cast<const uint16_t*>(reinterpret_cast<const uint8_t*>(lsp) + sdel_b);
+        }
       }
     } else {
       lleft = 0;
     }
   };
 
-  // ---- activation staging: piece idx -> (record, m, chunk, piece)
+  // ---- activation staging: piece idx -> (record, m, chunk, piece), over
+  // the padded row (CP chunks); pieces of chunks c >= C are zeros
   constexpr int XR = MR == 1 ? 1 : 4;  // pieces per thread per round
-  const int64_t per_slot = (int64_t)MR * C * PC;
+  const int64_t per_slot = (int64_t)MR * CP * PC;
   const int64_t P = nrec * per_slot;
   auto piece_of = [&](int64_t idx, int& slot, int& m, int64_t& c, int& t) __attribute__((always_inline)) {
     slot = (int)(idx / per_slot);
     int64_t rem = idx - (int64_t)slot * per_slot;
-    m = (int)(rem / ((int64_t)C * PC));
-    rem -= (int64_t)m * C * PC;
+    m = (int)(rem / ((int64_t)CP * PC));
+    rem -= (int64_t)m * CP * PC;
     c = rem / PC;
     t = (int)(rem - c * PC);
   };
@@ -322,6 +342,7 @@ __device__ __forceinline__ void run_segment(const StreamPhase& seg, const Stream
       int slot, m, t;
       int64_t c;
       piece_of(idx, slot, m, c, t);
+      if (c >= C) c = 0;  // padding: a valid address, zeroed when stored
       const uint16_t* xr = rec[slot].x + (int64_t)m * rec[slot].ldx + c * WPC;
       if constexpr (BITS == 4 || BITS == 8) {
         xraw[i] = load_x16(xr + 8 * t, coherent);
@@ -349,7 +370,9 @@ __device__ __forceinline__ void run_segment(const StreamPhase& seg, const Stream
       int slot, m, t;
       int64_t c;
       piece_of(live ? idx : 0, slot, m, c, t);
-      const uint32_t a0 = xraw[i][0], a1 = xraw[i][1], a2 = xraw[i][2], a3 = xraw[i][3];
+      const bool pad = c >= C;
+      const uint32_t a0 = pad ? 0u : xraw[i][0], a1 = pad ? 0u : xraw[i][1];
+      const uint32_t a2 = pad ? 0u : xraw[i][2], a3 = pad ? 0u : xraw[i][3];
       uint16_t v[8];
       if constexpr (BITS == 4) {  // decoder order (0,4,1,5,2,6,3,7)
         v[0] = a0 & 0xFFFF; v[1] = a2 & 0xFFFF; v[2] = a0 >> 16; v[3] = a2 >> 16;

@@ -26,6 +26,12 @@ QWEN25_7B = [
     ("gate", 18944, 3584), ("up", 18944, 3584), ("down", 3584, 18944),
 ]
 QWEN25_7B_LAYERS = 28
+# one rank's share of the 7B projections under 4-way tensor parallelism:
+# q, k, v, gate, up split by output rows, o and down by input columns
+QWEN25_7B_TP4 = [
+    ("q", 896, 3584), ("k", 128, 3584), ("v", 128, 3584), ("o", 3584, 896),
+    ("gate", 4736, 3584), ("up", 4736, 3584), ("down", 3584, 4736),
+]
 QWEN25_32B = [
     ("q", 5120, 5120), ("k", 1024, 5120), ("v", 1024, 5120), ("o", 5120, 5120),
     ("gate", 27648, 5120), ("up", 27648, 5120), ("down", 5120, 27648),
