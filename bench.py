@@ -44,13 +44,15 @@ SETTLE_S = 0.3               # untimed streaming before the warmup steps: clocks
 # HBM bytes per launch of the plan kernel from two rocprofv3 --pmc runs
 # (FETCH_SIZE, then WRITE_SIZE), each scaled by what that counter reads for a
 # 1 GiB device copy (FETCH_SIZE x 2.0, WRITE_SIZE x 1.0); the summary and the
-# commands are in profiles/gemv_stream_qwen7b_decode_m1.md. A figure holds only
+# commands are in profiles/gemv_stream_qwen7b*_m1.md. A figure holds only
 # for the kernel sources it was taken with (sha256 of KERNEL_SOURCES, first 16
 # hex digits); for any other source the bench reports traffic as null.
 KERNEL_SOURCES = ("weight_quantized_amd/csrc/zq_stream_impl.hpp", "weight_quantized_amd/csrc/zq_device.hpp",
                   "weight_quantized_amd/csrc/zq_internal.hpp", "weight_quantized_amd/csrc/zq_stream_m1.hip",
                   "weight_quantized_amd/csrc/zq_stream.hip")
-TRAFFIC = {("qwen7b-decode", 1, "plan", "independent"): (3395131937, "a44e61b14e160daf")}
+TRAFFIC = {("qwen7b-decode", 1, "plan", "independent"): (3395309158, "a6669e5147eb435a"),
+           ("qwen7b-decode-tp4", 1, "plan", "independent"): (881111040, "a6669e5147eb435a"),
+           ("qwen7b-decode-asym", 1, "plan", "independent"): (3504082739, "a6669e5147eb435a")}
 
 
 def kernel_source_hash() -> str:

@@ -320,7 +320,7 @@ struct zq_plan_s {
   bool waits = false;  // some segment waits for an earlier phase
   bool mfma = false;   // the MFMA batched-decode kernel (m >= MSTREAM_MIN_M)
   int64_t m = 1;
-  int variant = 12;  // one format for all segments, or 12 for a mix
+  int variant = 0;  // the kernel variant of the plan's one format, or the mixed-format one
   size_t lds = 0;
 };
 
