@@ -75,7 +75,8 @@ def parse():
                             "qwen7b-decode-asym", "qwen7b-decode-tp4", "hbm-copy"])
     p.add_argument("--m", type=int, default=None, help="activation rows (qwen7b-batch)")
     p.add_argument("--launch", default=None, choices=["plan", "graph", "eager"],
-                   help="plan: one resident launch per step (m <= 32, the default there); "
+                   help="plan (the default): one resident launch per step (m <= 32), or one "
+                        "persistent launch per bit width over a tile queue (prefill); "
                         "graph: the per-projection launches replayed as a HIP graph")
     p.add_argument("--order", default="independent", choices=["chained", "independent"],
                    help="plan phases: independent = every product of the step at once (each has its "
@@ -302,7 +303,7 @@ def main():
     stack = Stack(a.config, a.m, a.layers, torch, zq, synth)
 
     if a.launch is None:
-        a.launch = "plan" if stack.m <= 32 else "graph"
+        a.launch = "plan"  # m <= 32: the decode kernels; m > 64: the prefill tile queue
     # ---- timed region
     graph = None
     if a.launch == "plan":

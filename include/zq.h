@@ -234,7 +234,15 @@ zq_status zq_gemm(const zq_weight* W, const void* X, zq_dtype x_dtype, int64_t m
  *              streamed as one row space (any number of them, wherever they
  *              sit in the phase), split evenly over the workgroups.
  * zq_plan_create  validates every problem (as zq_gemm does) and requires
- *              1 <= m <= 32 (ZQ_ERR_UNSUPPORTED otherwise). For m >= 2, when
+ *              1 <= m <= 32, or m > 64 (ZQ_ERR_UNSUPPORTED otherwise).
+ *              m > 64 (prefill): every problem one scale per tensor,
+ *              symmetric codes, k a multiple of 64, 16-byte aligned codes
+ *              and activations, one x dtype and one phase; the plan runs one
+ *              persistent launch per bit width present, whose workgroups take
+ *              256 x 256 output tiles from per-XCD device counters, so one
+ *              run leaves no launch gaps between products and no idle CUs
+ *              until its last round. Results are those of zq_gemm, bit for
+ *              bit. For 2 <= m <= 32, when
  *              every problem is INT4 with k a multiple of 512, 16-byte aligned
  *              codes and activations and 8-byte aligned scales, the plan runs
  *              on the MFMA kernel; otherwise (m <= 4 only) on the vector-ALU
@@ -242,8 +250,9 @@ zq_status zq_gemm(const zq_weight* W, const void* X, zq_dtype x_dtype, int64_t m
  *              pointers and activations of one problem
  *              that fit in the 160 KiB of LDS with their group sums (m * k * 2
  *              bytes plus 1/32 of that). The plan
- *              copies the list to device memory and allocates three device
- *              words (phase counter, error word, finished workgroups).
+ *              copies the list to device memory and allocates a few device
+ *              words (phase or tile counters, error word, finished
+ *              workgroups).
  *              Pointers inside the problems are used at every run: the caller
  *              keeps those buffers alive.
  * zq_plan_run  enqueues the plan on `stream`: one launch with one workgroup

@@ -8,7 +8,7 @@ and activation rows are copied back and recomputed by the fp64 oracle.
     Qwen2.5-32B decode stack  (64 layers x 7, M = 1), plan
     7B stack, M = 8 and 32 (bf16 x), plan (MFMA batched-decode kernel)
     7B prefill stack (per-layer INT2/4/8, per-tensor scale, M = 2048, bf16 x),
-    graph over 4 streams
+    plan (tile queues) and graph over 4 streams
 """
 import os
 import sys
@@ -137,6 +137,17 @@ def test_qwen7b_batch_plan(mods, m):
     stack = bench.Stack("qwen7b-batch", m, None, torch, zq, synth)
     run_step(bench, stack, "plan")
     check_sampled(stack, n_rows=4)
+
+
+def test_qwen7b_prefill_plan(mods):
+    # the bench's default prefill launch: one persistent launch per bit width
+    bench, zq = mods
+    stack = bench.Stack("qwen7b-prefill", None, None, torch, zq, synth)
+    run_step(bench, stack, "plan")
+    run_step(bench, stack, "plan")  # the tile counters are back at zero
+    check_sampled(stack, n_rows=3, m_rows=3, seed=5)
+    del stack
+    torch.cuda.empty_cache()
 
 
 def test_qwen7b_prefill_graph_streams(mods):

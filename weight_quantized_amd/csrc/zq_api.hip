@@ -322,6 +322,13 @@ struct zq_plan_s {
   int64_t m = 1;
   int variant = 0;  // the kernel variant of the plan's one format, or the mixed-format one
   size_t lds = 0;
+  // prefill plans (m > 64): one tile queue per bit width, run in turn
+  bool prefill = false;
+  zq::PrefillProblem* pprobs = nullptr;  // device, grouped by bit width
+  int xt = 0;
+  int ngroup = 0;
+  int gfirst[3] = {0, 0, 0}, gcount[3] = {0, 0, 0}, gbits[3] = {0, 0, 0};
+  int64_t gtotal[3] = {0, 0, 0};  // tiles
 };
 
 namespace {
@@ -342,6 +349,100 @@ void seg_ranges(const zq::StreamPhase& sg, const std::vector<zq::StreamProblem>&
     out.push_back(make_int2(lo, hi));
   }
 }
+
+// A prefill plan (m > 64): every product per-tensor scaled, k a multiple of
+// 64, 16-byte aligned codes and activations, one activation type, one phase.
+zq_status create_prefill_plan(const zq_problem* problems, int count, int64_t m, zq_plan* plan_out) {
+  std::vector<zq::PrefillProblem> pp(count);
+  std::vector<int> order(count);
+  for (int i = 0; i < count; ++i) {
+    const zq_problem& q = problems[i];
+    zq_status st = check_weight(&q.w);
+    if (st) return fail(st, "problem %d: %s", i, g_err);
+    if (q.x_dtype != ZQ_F16 && q.x_dtype != ZQ_BF16)
+      return fail(ZQ_ERR_INVALID_ARG, "problem %d: x_dtype must be F16 or BF16", i);
+    if (q.y_dtype != ZQ_F32 && q.y_dtype != ZQ_F16 && q.y_dtype != ZQ_BF16)
+      return fail(ZQ_ERR_INVALID_ARG, "problem %d: y_dtype must be F32, F16 or BF16", i);
+    if (q.ldx < q.w.k || q.ldy < q.w.n) return fail(ZQ_ERR_INVALID_ARG, "problem %d: ldx < k or ldy < n", i);
+    if (q.w.n == 0 || q.w.k == 0 || !q.x || !q.y)
+      return fail(ZQ_ERR_UNSUPPORTED, "problem %d: empty shapes and null pointers are not planned", i);
+    if (q.x_dtype != problems[0].x_dtype)
+      return fail(ZQ_ERR_UNSUPPORTED, "problem %d: a prefill plan takes one activation type", i);
+    if (q.phase != problems[0].phase)
+      return fail(ZQ_ERR_UNSUPPORTED, "problem %d: a prefill plan has one phase", i);
+    zq::GemmArgs a{};
+    a.packed = (const uint8_t*)q.w.packed;
+    a.scales = q.w.scales;
+    a.zeros = q.w.zeros;
+    a.bits = q.w.bits;
+    a.group = q.w.group;
+    a.n = q.w.n;
+    a.k = q.w.k;
+    a.x = (const uint16_t*)q.x;
+    a.m = m;
+    a.ldx = q.ldx;
+    if (!zq::prefill_plan_supported(a))
+      return fail(ZQ_ERR_UNSUPPORTED, "problem %d: prefill plans need one scale per tensor, symmetric codes, k a "
+                  "multiple of 64 and 16-byte aligned codes and activations", i);
+    zq::PrefillProblem& p = pp[i];
+    p = zq::PrefillProblem{};
+    p.packed = a.packed;
+    p.scales = a.scales;
+    p.x = a.x;
+    p.y = q.y;
+    p.m = m;
+    p.n = q.w.n;
+    p.k = q.w.k;
+    p.ldx = q.ldx;
+    p.ldy = q.ldy;
+    p.mtiles = (m + zq::PREFILL_TILE - 1) / zq::PREFILL_TILE;
+    p.bits = q.w.bits;
+    p.yt = q.y_dtype == ZQ_F32 ? zq::YF32 : q.y_dtype == ZQ_F16 ? zq::YF16 : zq::YBF16;
+    order[i] = i;
+  }
+  // one queue per bit width (a kernel per width); within it the longest
+  // tiles first, so the last round of the queue is made of short ones
+  std::stable_sort(order.begin(), order.end(), [&](int u, int v) {
+    return pp[u].bits != pp[v].bits ? pp[u].bits < pp[v].bits : pp[u].k > pp[v].k;
+  });
+  std::vector<zq::PrefillProblem> sorted(count);
+  zq_plan_s* plan = new zq_plan_s;
+  plan->prefill = true;
+  plan->m = m;
+  plan->xt = problems[0].x_dtype == ZQ_F16 ? zq::XF16 : zq::XBF16;
+  int64_t total = 0;
+  for (int i = 0; i < count; ++i) {
+    sorted[i] = pp[order[i]];
+    if (i == 0 || sorted[i].bits != sorted[i - 1].bits) {
+      plan->gfirst[plan->ngroup] = i;
+      plan->gbits[plan->ngroup] = sorted[i].bits;
+      ++plan->ngroup;
+      total = 0;
+    }
+    sorted[i].tile0 = total;
+    total += sorted[i].mtiles * ((sorted[i].n + zq::PREFILL_TILE - 1) / zq::PREFILL_TILE);
+    plan->gcount[plan->ngroup - 1] += 1;
+    plan->gtotal[plan->ngroup - 1] = total;
+    if (total >= (int64_t)1 << 31) {
+      delete plan;
+      return fail(ZQ_ERR_UNSUPPORTED, "too many tiles in one plan");
+    }
+  }
+  hipError_t e = hipMalloc(&plan->pprobs, sizeof(zq::PrefillProblem) * count);
+  const size_t sync_bytes = 3 * zq::PREFILL_SYNC_WORDS * sizeof(uint32_t);
+  if (e == hipSuccess) e = hipMalloc(&plan->sync, sync_bytes);
+  if (e == hipSuccess)
+    e = hipMemcpy(plan->pprobs, sorted.data(), sizeof(zq::PrefillProblem) * count, hipMemcpyHostToDevice);
+  if (e == hipSuccess) e = hipMemset(plan->sync, 0, sync_bytes);
+  if (e != hipSuccess) {
+    (void)hipFree(plan->pprobs);
+    (void)hipFree(plan->sync);
+    delete plan;
+    return hip_fail(e, "plan allocation");
+  }
+  *plan_out = plan;
+  return ok();
+}
 }  // namespace
 
 extern "C" {
@@ -350,7 +451,9 @@ zq_status zq_plan_create(const zq_problem* problems, int count, int64_t m, zq_pl
   if (!plan_out) return fail(ZQ_ERR_INVALID_ARG, "null plan_out");
   *plan_out = nullptr;
   if (count < 1 || !problems) return fail(ZQ_ERR_INVALID_ARG, "empty problem list");
-  if (m < 1 || m > 32) return fail(ZQ_ERR_UNSUPPORTED, "plans take 1 <= m <= 32 (m=%lld)", (long long)m);
+  if (m > 64) return create_prefill_plan(problems, count, m, plan_out);
+  if (m < 1 || m > 32)
+    return fail(ZQ_ERR_UNSUPPORTED, "plans take 1 <= m <= 32, or m > 64 for prefill (m=%lld)", (long long)m);
   // the MFMA kernel when every product suits it; for m <= 4 the vector-ALU
   // kernel takes the other formats
   bool mfma = m >= zq::MSTREAM_MIN_M;
@@ -524,6 +627,13 @@ zq_status zq_plan_create(const zq_problem* problems, int count, int64_t m, zq_pl
 
 zq_status zq_plan_run(zq_plan plan, void* stream) {
   if (!plan) return fail(ZQ_ERR_INVALID_ARG, "null plan");
+  if (plan->prefill) {
+    hipError_t e = hipSuccess;
+    for (int g = 0; g < plan->ngroup && e == hipSuccess; ++g)
+      e = zq::launch_prefill_plan(plan->pprobs + plan->gfirst[g], plan->gcount[g], plan->gtotal[g], plan->xt,
+                                  plan->gbits[g], plan->sync + zq::PREFILL_SYNC_WORDS * g, (hipStream_t)stream);
+    return e == hipSuccess ? ok() : hip_fail(e, "plan launch");
+  }
   hipError_t e = plan->mfma
                      ? zq::launch_mstream_plan(plan->segs, plan->nseg, plan->probs, plan->ranges, plan->m,
                                                plan->variant, plan->lds, plan->sync, plan->waits, (hipStream_t)stream)
@@ -538,6 +648,7 @@ zq_status zq_plan_check(zq_plan plan) {
   hipError_t e = hipDeviceSynchronize();
   if (e == hipSuccess) e = hipMemcpy(w, plan->sync, sizeof w, hipMemcpyDeviceToHost);
   if (e != hipSuccess) return hip_fail(e, "plan check");
+  if (plan->prefill) return ok();  // no phase waits (its words are tile counters)
   if (w[1]) return fail(ZQ_ERR_HIP, "a phase wait gave up: outputs of that run are invalid");
   return ok();
 }
@@ -548,6 +659,7 @@ zq_status zq_plan_destroy(zq_plan plan) {
   hipError_t e1 = hipFree(plan->segs);
   if (e1 == hipSuccess) e1 = hipFree(plan->probs);
   if (e1 == hipSuccess) e1 = hipFree(plan->ranges);
+  if (e1 == hipSuccess) e1 = hipFree(plan->pprobs);
   hipError_t e2 = hipFree(plan->sync);
   delete plan;
   if (e != hipSuccess) return hip_fail(e, "plan destroy sync");

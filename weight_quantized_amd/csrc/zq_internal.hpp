@@ -86,6 +86,25 @@ hipError_t launch_gemv_valu(const GemmArgs& a);
 // prefill MFMA kernel: m > 64, one scale per tensor, k a multiple of 64
 bool gemm_prefill2_supported(const GemmArgs& a);
 hipError_t launch_gemm_prefill2(const GemmArgs& a);
+// One product of a prefill plan (device pointers): its 256 x 256 tiles are
+// plan tiles [tile0, tile0 + mtiles * ntiles), row block fastest.
+struct PrefillProblem {
+  const uint8_t* packed;
+  const uint16_t* scales;
+  const uint16_t* x;
+  void* y;
+  int64_t m, n, k, ldx, ldy;
+  int64_t tile0, mtiles;
+  int32_t bits, yt;
+};
+constexpr int PREFILL_TILE = 256;
+bool prefill_plan_supported(const GemmArgs& a);
+// persistent launch over the `total` tiles of products of one bit width;
+// xt: their activations' type; sync: PREFILL_SYNC_WORDS device words (tile
+// counters, finished workgroups), zero before the first run
+constexpr int PREFILL_SYNC_WORDS = 16;
+hipError_t launch_prefill_plan(const PrefillProblem* dev_probs, int nprob, int64_t total, int xt, int bits,
+                               uint32_t* sync, hipStream_t stream);
 // MFMA kernels for larger m
 bool gemm_mfma_supported(const GemmArgs& a);
 hipError_t launch_gemm_mfma(const GemmArgs& a);

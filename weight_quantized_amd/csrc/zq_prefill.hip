@@ -27,6 +27,8 @@
 //     x * (q + BIAS) with matching pairs;
 //   * every activation row's sum over K is accumulated while staging; the
 //     epilogue stores s * (acc - BIAS * rowsum).
+#include <algorithm>
+
 #include "zq_device.hpp"
 #include "zq_internal.hpp"
 
@@ -100,22 +102,28 @@ __device__ __forceinline__ u4 p2_bfrag(const u4 (&c)[2], int kk) {
   }
 }
 
+// One 256 x 256 tile of Y (rows m0.., columns n0..) by the workgroup's
 // WGM x WGN waves; wave (wm, wn) computes rows 256/WGM * wm.. and columns
-// 256/WGN * wn.. of the tile as FI x FJ MFMA 32x32 tiles.
+// 256/WGN * wn.. of the tile as FI x FJ MFMA 32x32 tiles. Uses P2_LDS bytes
+// of `smem`; ends with every wave past its last LDS access.
 template <int XT, int BITS, int WGM, int WGN>
-__global__ __launch_bounds__(64 * WGM * WGN) void gemm_prefill2_kernel(
-    const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales, int64_t n, int64_t k,
-    const uint16_t* __restrict__ x, int64_t m, int64_t ldx, void* __restrict__ y, int64_t ldy, int yt) {
-  extern __shared__ __align__(16) uint8_t smem[];
+__device__ __forceinline__ void p2_tile(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales,
+                                        int64_t n, int64_t k, const uint16_t* __restrict__ x, int64_t m, int64_t ldx,
+                                        void* __restrict__ y, int64_t ldy, int yt, int64_t m0, int64_t n0,
+                                        uint8_t* smem) {
   constexpr int NT = 64 * WGM * WGN;
   constexpr int TM = P2_BM / WGM, TN = P2_BN / WGN, FI = TM / 32, FJ = TN / 32;
   constexpr int SPT = 1024 / NT;            // 16-k activation spans per thread per step
   constexpr int CB = 8 * BITS;              // code bytes of one row per 64-k step
   constexpr int NB = BITS == 8 ? 2 : 1;     // 16-byte code loads per lane per fragment
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // the thread index goes through an empty asm: in the persistent plan
+  // kernel this keeps lane-dependent offsets from being hoisted out of the
+  // tile loop, where they would hold registers across it (and spill)
+  int tid_ = threadIdx.x;
+  __asm__ volatile("" : "+v"(tid_));
+  const int tid = tid_, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WGN, wn = wave % WGN;
   const int g = lane >> 5;
-  const int64_t m0 = (int64_t)blockIdx.y * P2_BM, n0 = (int64_t)blockIdx.x * P2_BN;
   const int64_t rowbytes = k * BITS / 8;
   const int64_t KT = k / P2_BK;
   float* rowsum = reinterpret_cast<float*>(smem + 2 * P2_TILE);
@@ -263,6 +271,78 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_prefill2_kernel(
       }
     }
   }
+  __syncthreads();  // the row sums are read: the next tile may reuse the LDS
+}
+
+template <int XT, int BITS, int WGM, int WGN>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_prefill2_kernel(
+    const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales, int64_t n, int64_t k,
+    const uint16_t* __restrict__ x, int64_t m, int64_t ldx, void* __restrict__ y, int64_t ldy, int yt) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  p2_tile<XT, BITS, WGM, WGN>(packed, scales, n, k, x, m, ldx, y, ldy, yt, (int64_t)blockIdx.y * P2_BM,
+                              (int64_t)blockIdx.x * P2_BN, smem);
+}
+
+// Prefill plan: the tiles of many products of one bit width in one persistent
+// launch (one workgroup per CU). Plan order lists products by decreasing k,
+// each product's tiles with the row block fastest. Tile t belongs to queue
+// t % 8, one queue per XCD: with 8 row blocks (m = 2048) an XCD then runs one
+// row block of every product, so its activation rows stay in its own L2,
+// and the last round of each queue is made of short tiles. A workgroup takes
+// tiles from its XCD's queue (a device counter), then from the others' until
+// all are empty, so every tile is computed whatever the grid. The last
+// workgroup to finish leaves the counters at zero for the next run.
+constexpr int PP_QUEUES = 8;
+
+template <int XT, int BITS, int WGM, int WGN>
+__global__ __launch_bounds__(64 * WGM * WGN) void gemm_prefill_plan_kernel(const PrefillProblem* __restrict__ probs,
+                                                                           int nprob, int64_t total,
+                                                                           uint32_t* __restrict__ sync) {
+  extern __shared__ __align__(16) uint8_t smem[];
+  __shared__ int s_tile;  // tiles of one plan stay below 2^31
+  __shared__ int s_prob;
+  const int xcc = (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & (PP_QUEUES - 1));  // HW_REG_XCC_ID
+  int q = 0;  // queues tried so far, starting with this XCD's
+  for (;;) {
+    if (threadIdx.x == 0) {
+      int64_t t = total;
+      while (q < PP_QUEUES) {
+        const int qi = (xcc + q) & (PP_QUEUES - 1);
+        const int64_t j = (int64_t)__hip_atomic_fetch_add(sync + qi, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        t = qi + PP_QUEUES * j;
+        if (t < total) break;
+        ++q;  // this queue is empty
+      }
+      int p = 0;
+      if (t < total) {
+        int lo = 0, hi = nprob - 1;  // last product whose first tile is <= t
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) / 2;
+          if (probs[mid].tile0 <= t) lo = mid;
+          else hi = mid - 1;
+        }
+        p = lo;
+      }
+      s_tile = (int)(t < total ? t : total);
+      s_prob = p;
+    }
+    __syncthreads();
+    // uniform values: read into scalar registers, so the tile's addressing
+    // stays scalar (LDS reads are taken as per-lane values otherwise)
+    const int64_t t = (int64_t)__builtin_amdgcn_readfirstlane(s_tile);
+    const int pi = __builtin_amdgcn_readfirstlane(s_prob);
+    __syncthreads();  // read before thread 0 takes the next tile
+    if (t >= total) break;
+    const PrefillProblem& pr = probs[pi];
+    const int local = (int)(t - pr.tile0), mt = (int)pr.mtiles;
+    const int nb = local / mt, mb = local - nb * mt;
+    p2_tile<XT, BITS, WGM, WGN>(pr.packed, pr.scales, pr.n, pr.k, pr.x, pr.m, pr.ldx, pr.y, pr.ldy, pr.yt,
+                                (int64_t)mb * P2_BM, (int64_t)nb * P2_BN, smem);
+  }
+  if (threadIdx.x == 0 &&
+      __hip_atomic_fetch_add(sync + PP_QUEUES, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1) {
+    for (int i = 0; i <= PP_QUEUES; ++i) __hip_atomic_store(sync + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 bool gemm_prefill2_supported(const GemmArgs& a) {
@@ -286,6 +366,33 @@ static hipError_t p2_launch(const GemmArgs& a) {
   hipLaunchKernelGGL((gemm_prefill2_kernel<XT, BITS, WGM, WGN>), grid, dim3(64 * WGM * WGN), P2_LDS, a.stream,
                      a.packed, a.scales, a.n, a.k, a.x, a.m, a.ldx, a.y, a.ldy, a.yt);
   return hipGetLastError();
+}
+
+bool prefill_plan_supported(const GemmArgs& a) { return a.zeros == nullptr && gemm_prefill2_supported(a); }
+
+template <int XT, int BITS>
+static hipError_t pp_launch(const PrefillProblem* dev_probs, int nprob, int64_t total, uint32_t* sync,
+                            hipStream_t stream) {
+  constexpr int WGM = ZQ_P2_WGM, WGN = ZQ_P2_WGN;
+  const void* fn = reinterpret_cast<const void*>(&gemm_prefill_plan_kernel<XT, BITS, WGM, WGN>);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, P2_LDS);
+  if (e != hipSuccess) return e;
+  const int64_t G = std::min<int64_t>(stream_grid(), total);
+  hipLaunchKernelGGL((gemm_prefill_plan_kernel<XT, BITS, WGM, WGN>), dim3((unsigned)G), dim3(64 * WGM * WGN),
+                     P2_LDS, stream, dev_probs, nprob, total, sync);
+  return hipGetLastError();
+}
+
+hipError_t launch_prefill_plan(const PrefillProblem* dev_probs, int nprob, int64_t total, int xt, int bits,
+                               uint32_t* sync, hipStream_t stream) {
+  if (xt == XF16) {
+    if (bits == 2) return pp_launch<XF16, 2>(dev_probs, nprob, total, sync, stream);
+    if (bits == 4) return pp_launch<XF16, 4>(dev_probs, nprob, total, sync, stream);
+    return pp_launch<XF16, 8>(dev_probs, nprob, total, sync, stream);
+  }
+  if (bits == 2) return pp_launch<XBF16, 2>(dev_probs, nprob, total, sync, stream);
+  if (bits == 4) return pp_launch<XBF16, 4>(dev_probs, nprob, total, sync, stream);
+  return pp_launch<XBF16, 8>(dev_probs, nprob, total, sync, stream);
 }
 
 hipError_t launch_gemm_prefill2(const GemmArgs& a) {
