@@ -84,23 +84,49 @@ __device__ __forceinline__ float p2_sum8(const u4& p, float acc) {
 // INT4: one u4, INT8: two u4, INT2: one u2 (in a u4, upper half unused);
 // step kk takes codes 8kk .. 8kk+7 of them, decoded in pair order, which
 // matches activation piece kc = 4g + kk staged by p2_perm.
+//
+// bf16 INT2 / INT4: a pair (code i, code i + E/2) of a dword moves, by one
+// shift, to bits 0.. of each 16-bit half; there it is the low fraction bits
+// of the bf16 number 128, whose unit in the last place is 1: (t & M) | 0x4300
+// is the exact value 128 + u, u = q + 2^(b-1) the code with its sign bit
+// flipped. The flip folds into the masking, ((t ^ S) & M) | O ==
+// (t & M) ^ ((S & M) ^ O): a shift and one v_bitop3 per pair. BIAS =
+// 128 + 2^(b-1) is removed in the epilogue. fp16 activations keep the
+// decoder with the smaller offset 16 + u: with 1024 + u the fp32 sums of
+// long rows would carry ten more bits of offset.
+// INT8 (256 code values do not fit a bf16 fraction): byte -> float -> the
+// upper 16 bits, exact; BIAS = 128.
 template <int XT, int BITS>
-__device__ __forceinline__ u4 p2_bfrag(const u4 (&c)[2], int kk) {
-  using Dc = Decoder<XT, BITS>;
-  constexpr uint32_t S = Codes<BITS>::SIGNS;
-  if constexpr (BITS == 4) {
-    const uint32_t v = c[0][kk] ^ S;
-    return u4{Dc::template pair<0>(v), Dc::template pair<1>(v), Dc::template pair<2>(v), Dc::template pair<3>(v)};
-  } else if constexpr (BITS == 8) {
-    const uint32_t v0 = c[kk >> 1][2 * (kk & 1)] ^ S, v1 = c[kk >> 1][2 * (kk & 1) + 1] ^ S;
-    return u4{Dc::template pair<0>(v0), Dc::template pair<1>(v0), Dc::template pair<0>(v1), Dc::template pair<1>(v1)};
-  } else {
-    const uint32_t v = c[0][kk >> 1] ^ S;
-    if (kk & 1)
-      return u4{Dc::template pair<4>(v), Dc::template pair<5>(v), Dc::template pair<6>(v), Dc::template pair<7>(v)};
-    return u4{Dc::template pair<0>(v), Dc::template pair<1>(v), Dc::template pair<2>(v), Dc::template pair<3>(v)};
+struct P2Dec {
+  static constexpr bool FAST = XT == XBF16 && BITS <= 4;
+  static constexpr float BIAS = FAST ? 128.f + (float)(1 << (BITS - 1)) : Decoder<XT, BITS>::BIAS;
+  static constexpr uint32_t M = BITS == 4 ? 0x000F000Fu : 0x00030003u;
+  static constexpr uint32_t K = (BITS == 4 ? 0x00080008u : 0x00020002u) ^ 0x43004300u;
+
+  static __device__ __forceinline__ u4 frag(const u4 (&c)[2], int kk) {
+    using Dc = Decoder<XT, BITS>;
+    constexpr uint32_t S = Codes<BITS>::SIGNS;
+    if constexpr (FAST && BITS == 4) {
+      const uint32_t v = c[0][kk];
+      return u4{(v & M) ^ K, ((v >> 4) & M) ^ K, ((v >> 8) & M) ^ K, ((v >> 12) & M) ^ K};
+    } else if constexpr (FAST) {
+      const uint32_t v = c[0][kk >> 1] >> ((kk & 1) * 8);  // pairs 0..3 or 4..7
+      return u4{(v & M) ^ K, ((v >> 2) & M) ^ K, ((v >> 4) & M) ^ K, ((v >> 6) & M) ^ K};
+    } else if constexpr (BITS == 4) {
+      const uint32_t v = c[0][kk] ^ S;
+      return u4{Dc::template pair<0>(v), Dc::template pair<1>(v), Dc::template pair<2>(v), Dc::template pair<3>(v)};
+    } else if constexpr (BITS == 8) {
+      const uint32_t v0 = c[kk >> 1][2 * (kk & 1)] ^ S, v1 = c[kk >> 1][2 * (kk & 1) + 1] ^ S;
+      return u4{Dc::template pair<0>(v0), Dc::template pair<1>(v0), Dc::template pair<0>(v1),
+                Dc::template pair<1>(v1)};
+    } else {
+      const uint32_t v = c[0][kk >> 1] ^ S;
+      if (kk & 1)
+        return u4{Dc::template pair<4>(v), Dc::template pair<5>(v), Dc::template pair<6>(v), Dc::template pair<7>(v)};
+      return u4{Dc::template pair<0>(v), Dc::template pair<1>(v), Dc::template pair<2>(v), Dc::template pair<3>(v)};
+    }
   }
-}
+};
 
 // One 256 x 256 tile of Y (rows m0.., columns n0..) by the workgroup's
 // WGM x WGN waves; wave (wm, wn) computes rows 256/WGM * wm.. and columns
@@ -128,15 +154,15 @@ __device__ __forceinline__ void p2_tile(const uint8_t* __restrict__ packed, cons
   const int64_t KT = k / P2_BK;
   float* rowsum = reinterpret_cast<float*>(smem + 2 * P2_TILE);
 
-  // activation staging: spans (row = s/4, 16-k span s%4), s = it*NT + tid
+  // activation staging: spans (row = s/4, 16-k span s%4), s = it*NT + tid.
+  // Rows past m re-read row m - 1: they only feed output rows past m, which
+  // are not stored.
   const uint16_t* xrow[SPT];
-  bool xlive[SPT];
 #pragma unroll
   for (int it = 0; it < SPT; ++it) {
     const int s = it * NT + tid;
     const int64_t r = m0 + (s >> 2);
     xrow[it] = x + (r < m ? r : m - 1) * ldx + 16 * (s & 3);
-    xlive[it] = r < m;
   }
   // weight fragments of this wave: rows n0 + TN wn + 32 j + lane % 32, bytes
   // CB/2 * g of each step
@@ -147,7 +173,9 @@ __device__ __forceinline__ void p2_tile(const uint8_t* __restrict__ packed, cons
     wfr[j] = packed + (r < n ? r : n - 1) * rowbytes + (CB / 2) * g;
   }
 
-  // two register sets: tile kt + 2 is loaded while tile kt computes
+  // two register sets: tile kt + 2 is loaded while tile kt computes (codes
+  // loaded two steps ahead measured slower: the third set of registers
+  // costs more than the latency it hides)
   u4 xa0[SPT][2], xa1[SPT][2], wb0[FJ][2], wb1[FJ][2];
   float rs[SPT];
 #pragma unroll
@@ -176,8 +204,7 @@ __device__ __forceinline__ void p2_tile(const uint8_t* __restrict__ packed, cons
   // stage activation span `it` of a tile into LDS stage st
   auto stage_span = [&](uint8_t* st, const u4 (&xa)[SPT][2], int it) __attribute__((always_inline)) {
     const int s = it * NT + tid, r = s >> 2, sp = s & 3;
-    u4 p0 = xa[it][0], p1 = xa[it][1];
-    if (!xlive[it]) p0 = p1 = u4{0u, 0u, 0u, 0u};
+    const u4 p0 = xa[it][0], p1 = xa[it][1];
     rs[it] = p2_sum8<XT>(p1, p2_sum8<XT>(p0, rs[it]));
     u4 s0, s1;
     p2_perm<BITS>(p0, p1, s0, s1);
@@ -215,7 +242,7 @@ __device__ __forceinline__ void p2_tile(const uint8_t* __restrict__ packed, cons
       if (kk < 3) read_a(cur, kk + 1, an);
       u4 b[FJ];
 #pragma unroll
-      for (int j = 0; j < FJ; ++j) b[j] = p2_bfrag<XT, BITS>(wb[j], kk);
+      for (int j = 0; j < FJ; ++j) b[j] = P2Dec<XT, BITS>::frag(wb[j], kk);
 #pragma unroll
       for (int i = 0; i < FI; ++i)
 #pragma unroll
@@ -254,7 +281,7 @@ __device__ __forceinline__ void p2_tile(const uint8_t* __restrict__ packed, cons
   }
   __syncthreads();
 
-  using Dc = Decoder<XT, BITS>;
+  using Dc = P2Dec<XT, BITS>;
   const float s = f16_bits_to_float(scales[0]);
   // D layout of 32x32: value r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32
 #pragma unroll
