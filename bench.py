@@ -12,7 +12,8 @@ starts.
 
 Prints one JSON line. Other workloads (--config):
   gemv-512             single 512 x 512 INT4 GEMV, per-tensor scale fp16(0.02)
-  qwen7b-batch --m M   the 7B stack at M in {1,4,8,16,32}, bf16 activations
+  qwen7b-batch --m M   the 7B stack at M rows of bf16 activations (M <= 32: one
+                       plan launch; M > 32: 32-row chunks of it)
   qwen32b-decode       64 layers of Qwen2.5-32B projection shapes, M = 1
   qwen7b-decode-asym   the 7B decode stack with asymmetric INT4 weights (unsigned
                        codes, fp16 scale and zero point per 128-group)
@@ -387,6 +388,7 @@ def main():
         out.update({"value": round(gbs, 1), "unit": "GB/s", "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
                     "us_per_layer": round(per_layer_us, 3),
                     "tok_s_equiv": round(stack.m / (ms * 1e-3), 1),
+                    "tflop_s": round(stack.flops / (ms * 1e-3) / 1e12, 2),
                     "roofline": {"bound": "hbm", "achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS,
                                  "unit": "GB/s", "frac": round(kern_gbs / HBM_PEAK_GBS, 4),
                                  "traffic": traffic},

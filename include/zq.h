@@ -205,6 +205,8 @@ zq_status zq_gemv(const zq_weight* W, const void* x, zq_dtype x_dtype, void* y,
  *   m = 2..32, INT4, k a multiple of 512, 16-byte aligned codes and
  *     activations, 8-byte aligned scales: a resident MFMA kernel that streams
  *     the codes once;
+ *   m > 32, INT4 with group scales (per-tensor scales: m <= 64), k a
+ *     multiple of 512, aligned as above: that kernel on chunks of 32 rows;
  *   m > 64, one scale per tensor, k a multiple of 64: a tiled MFMA kernel
  *     (256 x 256 tiles) that decodes codes in registers;
  *   anything else: tiled MFMA kernels, or a general kernel for unaligned and
@@ -242,7 +244,11 @@ zq_status zq_gemm(const zq_weight* W, const void* X, zq_dtype x_dtype, int64_t m
  *              256 x 256 output tiles from per-XCD device counters, so one
  *              run leaves no launch gaps between products and no idle CUs
  *              until its last round. Results are those of zq_gemm, bit for
- *              bit. For 2 <= m <= 32, when
+ *              bit. 32 < m with group scales (or 32 < m <= 64 per tensor):
+ *              every problem INT4, k a multiple of 512, aligned as below; the
+ *              rows run in chunks of 32 (never a last chunk of one row),
+ *              each a plan of its own, so the weights stream once per chunk.
+ *              For 2 <= m <= 32, when
  *              every problem is INT4 with k a multiple of 512, 16-byte aligned
  *              codes and activations and 8-byte aligned scales, the plan runs
  *              on the MFMA kernel; otherwise (m <= 4 only) on the vector-ALU

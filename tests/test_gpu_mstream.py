@@ -155,3 +155,63 @@ def test_mstream_plan_rejects_other_formats():
     X33 = torch.zeros((33, 512), dtype=torch.float16, device=DEV)
     with pytest.raises(zq.ZqError):
         zq.Plan([(W4, X33, torch.empty((33, 64), device=DEV), 0)])
+
+
+# ---------------------------------------------------------------------------
+# mid-batch m (32 < m): 32-row chunks on the batched-decode kernel (group
+# scales at any m, per-tensor scales up to 64), single calls and plans
+
+
+def chunks(m):
+    out, r0 = [], 0
+    while r0 < m:
+        mc = 31 if m - r0 == 33 else min(32, m - r0)
+        out.append((r0, mc))
+        r0 += mc
+    return out
+
+
+@pytest.mark.parametrize("xdt", ["f16", "bf16"])
+@pytest.mark.parametrize("group", [0, 128])
+@pytest.mark.parametrize("m", [33, 48, 64, 65, 100])
+def test_midbatch_matches_oracle_and_row_chunks(xdt, group, m):
+    n, k = 300, 1024
+    seed = 40 * m + group + (xdt == "bf16")
+    q, s, p, W = weight(4, group, n, k, seed)
+    x = synth.normal(synth.rng(seed + 1), (m, k), xdt)
+    X = x_dev(x, xdt)
+    Y = zq.gemm(W, X)
+    torch.cuda.synchronize()
+    check(Y.double().cpu().numpy(), O.gemm(p, 4, s, group, n, k, x, xdt), x, xdt, q, group, s, what=f"m={m}")
+    if group or m <= 64:
+        for r0, mc in chunks(m):  # each chunk is a batched-decode call on those rows
+            assert torch.equal(Y[r0:r0 + mc], zq.gemm(W, X[r0:r0 + mc])), f"rows {r0}..{r0 + mc}"
+
+
+@pytest.mark.parametrize("m", [33, 64, 100])
+def test_midbatch_plan_matches_oracle_and_single_calls(m):
+    probs, refs = [], []
+    for i, (group, n, k) in enumerate([(128, 512, 1024), (0, 300, 512), (128, 1000, 1536)]):
+        q, s, p, W = weight(4, group, n, k, seed=800 + 10 * m + i)
+        x = synth.normal(synth.rng(850 + 10 * m + i), (m, k), "bf16")
+        Y = torch.full((m, n), float("nan"), device=DEV)
+        probs.append((W, x_dev(x, "bf16"), Y, 0))
+        refs.append((q, s, p, x, group, n, k))
+    plan = zq.Plan(probs)
+    for _ in range(2):
+        plan.run()
+        torch.cuda.synchronize()
+    plan.check()
+    for (W, X, Y, _), (q, s, p, x, group, n, k) in zip(probs, refs):
+        check(Y.double().cpu().numpy(), O.gemm(p, 4, s, group, n, k, x, "bf16"), x, "bf16", q, group, s,
+              what=f"n={n}")
+        for r0, mc in chunks(m):
+            assert torch.equal(Y[r0:r0 + mc], zq.gemm(W, X[r0:r0 + mc]))
+
+
+def test_midbatch_plan_rejects_other_formats():
+    _, _, _, W8 = weight(8, 128, 64, 512, seed=3)
+    X = torch.zeros((48, 512), dtype=torch.bfloat16, device=DEV)
+    with pytest.raises(zq.ZqError) as e:
+        zq.Plan([(W8, X, torch.empty((48, 64), device=DEV), 0)])
+    assert e.value.status == zq.ERR_UNSUPPORTED

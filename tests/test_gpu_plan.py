@@ -139,9 +139,10 @@ def test_plan_validation():
     with pytest.raises(zq.ZqError) as e:
         zq.Plan([(W, X, torch.empty((1, 64), device=DEV), 1), (W, X, torch.empty((1, 64), device=DEV), 0)])
     assert e.value.status == zq.ERR_INVALID_ARG
+    _, _, _, W8 = weight(8, 128, 64, 512, seed=3)  # m > 32 takes INT4 (chunks) or per-tensor (m > 64) only
     X33 = torch.zeros((33, 512), dtype=torch.float16, device=DEV)
     with pytest.raises(zq.ZqError) as e:
-        zq.Plan([(W, X33, torch.empty((33, 64), device=DEV), 0)])
+        zq.Plan([(W8, X33, torch.empty((33, 64), device=DEV), 0)])
     assert e.value.status == zq.ERR_UNSUPPORTED
 
 
