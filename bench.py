@@ -406,6 +406,10 @@ def main():
     }[a.config], "layers": stack.layers, "m": stack.m,
         "weight_bytes_per_step": stack.weight_bytes, "launch": a.launch, "order": a.order if a.launch == "plan" else "stream",
         "launches_per_step": 1 if a.launch == "plan" else len(stack.launches),
+        # kernels one plan run enqueues: one per bit width (prefill tile
+        # queues), one per 32-row chunk (m > 32 on the batched-decode kernel)
+        "kernels_per_plan_run": (len({W.bits for W, _, _ in stack.launches}) if stack.m > 64 and stack.group == 0
+                                 else -(-stack.m // 32) if stack.m > 32 else 1) if a.launch == "plan" else None,
         "wall_ms_per_step": round(wall_ms, 5), "avg_kernel_us": round(avg_launch_ms * 1e3, 3),
         "streams": a.streams if a.launch == "graph" else 1,
         "settle_s": SETTLE_S}
