@@ -426,7 +426,10 @@ __device__ __forceinline__ void run_segment(const StreamPhase& seg, const Stream
 #pragma unroll
   for (int u = 0; u < U0; ++u) next_chunk(buf[u], sbuf[u], zbuf[u]);
   if (sync) {
-    // weights and scales do not depend on earlier phases: already in flight
+    // weights and scales do not depend on earlier phases: the whole window
+    // goes out before the wait, so it streams while the earlier phase ends
+#pragma unroll
+    for (int u = U0; u < U; ++u) next_chunk(buf[u], sbuf[u], zbuf[u]);
     if (tid == 0) {
       uint32_t polls = 0;
       while (__hip_atomic_load(sync, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < wait_target) {
@@ -439,10 +442,12 @@ __device__ __forceinline__ void run_segment(const StreamPhase& seg, const Stream
     }
     __syncthreads();
     load_x_round(0);
-  }
-  store_x_round(0);
+    store_x_round(0);
+  } else {
+    store_x_round(0);
 #pragma unroll
-  for (int u = U0; u < U; ++u) next_chunk(buf[u], sbuf[u], zbuf[u]);
+    for (int u = U0; u < U; ++u) next_chunk(buf[u], sbuf[u], zbuf[u]);
+  }
   for (int64_t it0 = XR; it0 * NT < P; it0 += XR) {
     load_x_round(it0);
     store_x_round(it0);
