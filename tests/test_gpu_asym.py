@@ -124,7 +124,7 @@ def test_gemm_asym_matches_oracle(xdt, bits, m):
 
 
 @pytest.mark.parametrize("xdt", ["f16", "bf16"])
-@pytest.mark.parametrize("m", [1, 3, 8])
+@pytest.mark.parametrize("m", [1, 3, 8, 20, 40])
 def test_gemm_asym_integer_inputs_bit_exact(xdt, m):
     n, k, bits = 90, 3584, 4
     g = synth.rng(500 + m)
@@ -165,7 +165,54 @@ def test_plan_mixing_symmetric_and_asymmetric(m):
     for (W, X, Y, _), (kind, q, s, z, p, x, bits, n, k) in zip(probs, refs):
         if kind == "a":
             yref, wdeq = O.gemm_asym(p, bits, s, z, n, k, x, "f16"), O.dequant_asym(q, s, z)
-            assert torch.equal(zq.gemm(W, X), Y)  # one kernel for both (m <= 4, asymmetric)
+            if m == 1 or bits != 4:  # single calls of INT4 at m >= 2 take the MFMA kernel
+                assert torch.equal(zq.gemm(W, X), Y)
         else:
             yref, wdeq = O.gemm(p, bits, s, 128, n, k, x, "f16"), O.dequant(q, 128, s)
         check(Y.double().cpu().numpy(), yref, x, "f16", wdeq)
+
+
+@pytest.mark.parametrize("xdt", ["f16", "bf16"])
+@pytest.mark.parametrize("m", [2, 8, 16, 17, 32, 33, 48, 100])
+def test_gemm_asym_batched_mfma_matches_oracle(xdt, m):
+    # INT4 with k a multiple of 512 at m >= 2: the MFMA batched-decode kernel
+    # (in 32-row chunks past 32), zero points included per group
+    for n, k in [(300, 512), (257, 1536)]:
+        seed = 3000 + 10 * m + k % 89 + (xdt == "bf16")
+        q, s, z, p, W = asym_weight(4, n, k, seed)
+        x = synth.normal(synth.rng(seed + 1), (m, k), xdt)
+        Y = zq.gemm(W, x_dev(x, xdt))
+        torch.cuda.synchronize()
+        check(Y.double().cpu().numpy(), O.gemm_asym(p, 4, s, z, n, k, x, xdt), x, xdt, O.dequant_asym(q, s, z))
+
+
+@pytest.mark.parametrize("m", [8, 24, 40])
+def test_plan_asym_batched_matches_oracle_and_single_calls(m):
+    # an MFMA plan mixing asymmetric and symmetric INT4 products
+    probs, refs = [], []
+    for i, (kind, n, k) in enumerate([("a", 512, 1024), ("s", 300, 1024), ("a", 1000, 1536)]):
+        if kind == "a":
+            q, s, z, p, W = asym_weight(4, n, k, 90 + i)
+        else:
+            g = synth.rng(90 + i)
+            q = synth.codes_uniform(g, n, k, 4)
+            s = synth.scales_abs_normal(g, n * k // 128)
+            z, p = None, O.pack(q, 4)
+            W = zq.ZqWeight(4, 128, n, k, dev(p.reshape(-1)), dev(s.view(np.float16)))
+        x = synth.normal(synth.rng(95 + i), (m, k), "bf16")
+        Y = torch.full((m, n), float("nan"), device=DEV)
+        probs.append((W, x_dev(x, "bf16"), Y, 0))
+        refs.append((kind, q, s, z, p, x, n, k))
+    plan = zq.Plan(probs)
+    for _ in range(2):
+        plan.run()
+        torch.cuda.synchronize()
+    plan.check()
+    for (W, X, Y, _), (kind, q, s, z, p, x, n, k) in zip(probs, refs):
+        if kind == "a":
+            yref, wdeq = O.gemm_asym(p, 4, s, z, n, k, x, "bf16"), O.dequant_asym(q, s, z)
+        else:
+            yref, wdeq = O.gemm(p, 4, s, 128, n, k, x, "bf16"), O.dequant(q, 128, s)
+        check(Y.double().cpu().numpy(), yref, x, "bf16", wdeq)
+        if m <= 32:
+            assert torch.equal(zq.gemm(W, X), Y)  # same kernel, same per-row arithmetic

@@ -279,14 +279,15 @@ zq_status zq_gemm(const zq_weight* W, const void* X, zq_dtype x_dtype, int64_t m
   const int64_t rowbytes = W->k * W->bits / 8;
   const bool aligned16 = ((uintptr_t)W->packed & 15) == 0 && rowbytes % 16 == 0 &&
                          ((uintptr_t)X & 15) == 0 && (m == 1 || (ldx * 2) % 16 == 0);
-  // asymmetric weights: the vector-ALU stream kernel (m <= 4) or the general kernel
+  // asymmetric weights: the vector-ALU stream kernel (m = 1), the MFMA
+  // batched-decode kernel (INT4) or the general kernel
   const bool asym = W->zeros != nullptr;
-  const bool use_mstream = !asym && m >= zq::MSTREAM_MIN_M &&
-                           zq::mstream_supported(W->packed, W->scales, W->bits, W->group, m, W->k, X, ldx);
+  const bool use_mstream = m >= zq::MSTREAM_MIN_M &&
+                           zq::mstream_supported(W->packed, W->scales, W->zeros, W->bits, W->group, m, W->k, X, ldx);
   // mid-batch m (group scales: any m > 32; per tensor: up to 64, past which
   // the prefill kernel is faster): 32-row chunks on the batched-decode kernel
-  const bool use_chunks = !asym && m > 32 && (W->group != 0 || m <= 64) &&
-                          zq::mstream_supported(W->packed, W->scales, W->bits, W->group, 32, W->k, X, ldx);
+  const bool use_chunks = m > 32 && (W->group != 0 || m <= 64) &&
+                          zq::mstream_supported(W->packed, W->scales, W->zeros, W->bits, W->group, 32, W->k, X, ldx);
   if (use_chunks) {
     const int ysz = y_dtype == ZQ_F32 ? 4 : 2;
     e = hipSuccess;
@@ -295,6 +296,7 @@ zq_status zq_gemm(const zq_weight* W, const void* X, zq_dtype x_dtype, int64_t m
       zq::StreamProblem p{};
       p.packed = a.packed;
       p.scales = a.scales;
+      p.zeros = a.zeros;
       p.x = a.x + r0 * ldx;
       p.y = (uint8_t*)Y + r0 * ldy * ysz;
       p.n = a.n;
@@ -488,7 +490,7 @@ zq_status create_chunked_plan(const zq_problem* problems, int count, int64_t m, 
     const zq_problem& q = problems[i];
     zq_status st = check_weight(&q.w);
     if (st) return fail(st, "problem %d: %s", i, g_err);
-    if (q.w.zeros || !zq::mstream_supported(q.w.packed, q.w.scales, q.w.bits, q.w.group, 32, q.w.k, q.x, q.ldx))
+    if (!zq::mstream_supported(q.w.packed, q.w.scales, q.w.zeros, q.w.bits, q.w.group, 32, q.w.k, q.x, q.ldx))
       return fail(ZQ_ERR_UNSUPPORTED, "problem %d: plans with m > 32 need INT4 codes, k a multiple of 512, "
                   "16-byte aligned codes and activations and 8-byte aligned scales (or, for m > 64, one scale "
                   "per tensor)", i);
@@ -539,8 +541,7 @@ zq_status zq_plan_create(const zq_problem* problems, int count, int64_t m, zq_pl
   if (mfma && m <= 4) {
     for (int i = 0; i < count && mfma; ++i) {
       const zq_problem& q = problems[i];
-      mfma = !q.w.zeros &&
-             zq::mstream_supported(q.w.packed, q.w.scales, q.w.bits, q.w.group, m, q.w.k, q.x, q.ldx);
+      mfma = zq::mstream_supported(q.w.packed, q.w.scales, q.w.zeros, q.w.bits, q.w.group, m, q.w.k, q.x, q.ldx);
     }
   }
   std::vector<zq::StreamProblem> probs(count);
@@ -561,7 +562,7 @@ zq_status zq_plan_create(const zq_problem* problems, int count, int64_t m, zq_pl
     const bool aligned = ((uintptr_t)q.w.packed & 15) == 0 && ((uintptr_t)q.x & 15) == 0 &&
                          (m == 1 || (q.ldx * 2) % 16 == 0);
     if (mfma) {
-      if (q.w.zeros || !zq::mstream_supported(q.w.packed, q.w.scales, q.w.bits, q.w.group, m, q.w.k, q.x, q.ldx))
+      if (!zq::mstream_supported(q.w.packed, q.w.scales, q.w.zeros, q.w.bits, q.w.group, m, q.w.k, q.x, q.ldx))
         return fail(ZQ_ERR_UNSUPPORTED, "problem %d: plans with m > 4 need INT4 codes, k a multiple of 512, "
                     "16-byte aligned codes and activations and 8-byte aligned scales", i);
     } else if (!aligned || !zq::stream_supported(q.w.bits, q.w.group, m, q.w.n, q.w.k)) {
@@ -670,9 +671,9 @@ zq_status zq_plan_create(const zq_problem* problems, int count, int64_t m, zq_pl
   }
   int variant = -1;
   for (const zq::StreamPhase& sg : fitted) {
-    const int v = mfma ? zq::mstream_variant_of(sg.xt, sg.group)
+    const int v = mfma ? zq::mstream_variant_of(sg.xt, sg.group, sg.asym)
                        : zq::stream_variant_of(sg.xt, sg.bits, sg.group, sg.asym);
-    variant = (variant == -1 || variant == v) ? v : (mfma ? 4 : zq::STREAM_VAR_ANY);
+    variant = (variant == -1 || variant == v) ? v : (mfma ? zq::MSTREAM_VAR_ANY : zq::STREAM_VAR_ANY);
   }
   zq_plan_s* plan = new zq_plan_s;
   plan->nseg = (int)fitted.size();

@@ -71,10 +71,11 @@ hipError_t launch_stream_plan(const StreamPhase* dev_segs, int nseg, const Strea
 // multiple of 512, 16-byte aligned codes and activations, 8-byte aligned
 // group scales
 constexpr int MSTREAM_MIN_M = 2;  // measured faster than the VALU kernel from 2 rows on
-bool mstream_supported(const void* packed, const uint16_t* scales, int bits, int group, int64_t m, int64_t k,
-                       const void* x, int64_t ldx);
+bool mstream_supported(const void* packed, const uint16_t* scales, const uint16_t* zeros, int bits, int group,
+                       int64_t m, int64_t k, const void* x, int64_t ldx);
 size_t mstream_lds(int64_t m, int nrec);
-int mstream_variant_of(int xt, int group);  // 4 = a mix
+int mstream_variant_of(int xt, int group, int asym);
+constexpr int MSTREAM_VAR_ANY = 6;  // the variant of a plan that mixes formats
 hipError_t launch_mstream_single(const StreamProblem& p, int64_t m, hipStream_t stream);
 hipError_t launch_mstream_plan(const StreamPhase* dev_segs, int nseg, const StreamProblem* dev_probs,
                                const int2* dev_ranges, int64_t m, int variant, size_t lds, uint32_t* sync,

@@ -5,17 +5,19 @@
 
 namespace zq {
 
-bool mstream_supported(const void* packed, const uint16_t* scales, int bits, int group, int64_t m, int64_t k,
-                       const void* x, int64_t ldx) {
+bool mstream_supported(const void* packed, const uint16_t* scales, const uint16_t* zeros, int bits, int group,
+                       int64_t m, int64_t k, const void* x, int64_t ldx) {
   if (bits != 4 || m < 2 || m > 32 || k <= 0 || k % MS_KC != 0) return false;
   if (((uintptr_t)packed & 15) || ((uintptr_t)x & 15) || ((ldx * 2) & 15)) return false;
   if (group && ((uintptr_t)scales & 7)) return false;
+  if (zeros && (!group || ((uintptr_t)zeros & 7))) return false;
   return mstream_lds(m, 1) <= STREAM_LDS_MAX;
 }
 
 size_t mstream_lds(int64_t m, int nrec) { return mstream_lds_bytes(m <= 16 ? 1 : 2, nrec); }
 
-int mstream_variant_of(int xt, int group) { return mstream_variant(xt, group); }
+int mstream_variant_of(int xt, int group, int asym) { return mstream_variant(xt, group, asym); }
+static_assert(MVAR_ANY == MSTREAM_VAR_ANY, "the host and the kernels agree on the mixed-format variant");
 
 static const void* mstream_kernel_for(int64_t m, int var) {
   return m <= 16 ? mstream_kernel_t1(var) : mstream_kernel_t2(var);
@@ -35,9 +37,10 @@ hipError_t launch_mstream_single(const StreamProblem& p, int64_t m, hipStream_t 
   seg.bits = p.bits;
   seg.group = p.group;
   seg.xt = p.xt;
+  seg.asym = p.zeros ? 1 : 0;
   StreamProblem pp = p;
   pp.row_off = 0;
-  const void* fn = mstream_kernel_for(m, mstream_variant(p.xt, p.group));
+  const void* fn = mstream_kernel_for(m, mstream_variant(p.xt, p.group, seg.asym));
   const size_t lds = mstream_lds(m, 1);
   hipError_t e = ms_lds_attr(fn, lds);
   if (e != hipSuccess) return e;

@@ -49,8 +49,9 @@ constexpr int MS_TW = 2;         // 16-row tiles per wave per block
 constexpr int MS_BLOCK = 8 * MS_TW * 16;
 
 // LDS bytes of one activation chunk buffer: A fragments [gs][mt][d][g][m][8]
-// (16 bytes each) and the negated offset sums [gs][mt][m] (fp32).
-__host__ __device__ constexpr int mstream_xbuf_bytes(int mt) { return mt * (4 * 4 * 4 * 16 * 16 + 4 * 16 * 4); }
+// (16 bytes each), the negated offset sums [gs][mt][m] (fp32) and, for
+// asymmetric weights, the plain sums [gs][mt][m] (fp32).
+__host__ __device__ constexpr int mstream_xbuf_bytes(int mt) { return mt * (4 * 4 * 4 * 16 * 16 + 2 * 4 * 16 * 4); }
 // Weight transpose scratch of one wave: per tile, 4 loads x 4 rows x 16
 // pieces of 16 bytes, each 16-piece row padded by 16 bytes (272 bytes) so
 // that both the row-wise writes and the tile-column reads are conflict-free.
@@ -61,30 +62,35 @@ __host__ __device__ inline size_t mstream_lds_bytes(int mt, int nrec) {
   return (size_t)nrec * PROD_REC_BYTES + 2 * (size_t)mstream_xbuf_bytes(mt) + 8 * (size_t)MS_WSCR;
 }
 
-// INT4 decoder for the MFMA kernel: raw packed dword (codes not yet
-// sign-flipped) -> 4 dwords of packed 16-bit values, pair p holding codes
-// (p, p + 4) as u + magic, u = q + 8. The sign flip is folded into the mask:
-// ((v ^ S) & M) | O == (v & M) ^ ((S & M) ^ O).
+// INT4 decoder for the MFMA kernel: raw packed dword -> 4 dwords of packed
+// 16-bit values, pair p holding codes (p, p + 4) as u + magic, u = q + 8 for
+// signed codes (the sign flip folded into the mask: ((v ^ S) & M) | O ==
+// (v & M) ^ ((S & M) ^ O)) and u = the code itself for unsigned
+// (asymmetric) ones.
 //  fp16: pairs 0, 2 as 1024 + u (nibble in fraction bits 3:0), pairs 1, 3 as
-//        64 + u (nibble in bits 7:4, exponent 2^6); offsets 1032 / 72.
-//  bf16: every pair as 128 + u (nibble in fraction bits 3:0); offset 136.
-template <int XT>
+//        64 + u (nibble in bits 7:4, exponent 2^6); offsets 1032 / 72
+//        (asymmetric 1024 / 64).
+//  bf16: every pair as 128 + u (nibble in fraction bits 3:0); offset 136
+//        (asymmetric 128).
+template <int XT, bool ASYM = false>
 struct MDec {
-  static constexpr float BE = XT == XF16 ? 1032.f : 136.f;  // pairs of even k
-  static constexpr float BO = XT == XF16 ? 72.f : 136.f;    // pairs of odd k
+  static constexpr float FLIP = ASYM ? 0.f : 8.f;
+  static constexpr float BE = (XT == XF16 ? 1024.f : 128.f) + FLIP;  // pairs of even k
+  static constexpr float BO = (XT == XF16 ? 64.f : 128.f) + FLIP;    // pairs of odd k
+  static constexpr uint32_t S0 = ASYM ? 0u : 0x00080008u, S1 = ASYM ? 0u : 0x00800080u;
   static __device__ __forceinline__ u4 decode(uint32_t v) {
     u4 r;
     if constexpr (XT == XF16) {
       const uint32_t t = v >> 8;
-      r[0] = (v & 0x000F000Fu) ^ (0x00080008u ^ 0x64006400u);
-      r[1] = (v & 0x00F000F0u) ^ (0x00800080u ^ 0x54005400u);
-      r[2] = (t & 0x000F000Fu) ^ (0x00080008u ^ 0x64006400u);
-      r[3] = (t & 0x00F000F0u) ^ (0x00800080u ^ 0x54005400u);
+      r[0] = (v & 0x000F000Fu) ^ (S0 ^ 0x64006400u);
+      r[1] = (v & 0x00F000F0u) ^ (S1 ^ 0x54005400u);
+      r[2] = (t & 0x000F000Fu) ^ (S0 ^ 0x64006400u);
+      r[3] = (t & 0x00F000F0u) ^ (S1 ^ 0x54005400u);
     } else {
-      r[0] = (v & 0x000F000Fu) ^ (0x00080008u ^ 0x43004300u);
-      r[1] = ((v >> 4) & 0x000F000Fu) ^ (0x00080008u ^ 0x43004300u);
-      r[2] = ((v >> 8) & 0x000F000Fu) ^ (0x00080008u ^ 0x43004300u);
-      r[3] = ((v >> 12) & 0x000F000Fu) ^ (0x00080008u ^ 0x43004300u);
+      r[0] = (v & 0x000F000Fu) ^ (S0 ^ 0x43004300u);
+      r[1] = ((v >> 4) & 0x000F000Fu) ^ (S0 ^ 0x43004300u);
+      r[2] = ((v >> 8) & 0x000F000Fu) ^ (S0 ^ 0x43004300u);
+      r[3] = ((v >> 12) & 0x000F000Fu) ^ (S0 ^ 0x43004300u);
     }
     return r;
   }
@@ -103,12 +109,15 @@ __device__ __forceinline__ f4 ms_mfma(u4 a, u4 b, f4 c) {
 // (<= 16 * MT).
 // COH: activations and outputs cross phases (agent-coherent accesses); a
 // template parameter so the main loop has one fixed number of loads.
-template <int XT, bool GROUPED, int MT, bool COH>
+// ASYM: unsigned codes with a zero point per group (w = q * s + z): each
+// group adds z * (sum of the group's activations) to every output of its row.
+template <int XT, bool GROUPED, int MT, bool COH, bool ASYM = false>
 __device__ __forceinline__ void run_msegment(const StreamPhase& seg, const StreamProblem* probs,
                                              const StreamProblem& single, int2 wr, int m, uint8_t* smem,
                                              uint32_t* sync, uint32_t wait_target) {
+  static_assert(!ASYM || GROUPED, "zero points come per 128-group");
   constexpr bool coherent = COH;
-  using D = MDec<XT>;
+  using D = MDec<XT, ASYM>;
   constexpr int NT = MS_THREADS;
   constexpr int XB = mstream_xbuf_bytes(MT);
   constexpr int PPT = MT * 16 * 64 / NT;  // activation pieces (8 values) per thread per chunk
@@ -172,7 +181,7 @@ __device__ __forceinline__ void run_msegment(const StreamPhase& seg, const Strea
   // Loads are unconditional (tiles past a block's end re-read its last row),
   // so the compiler counts them exactly.
   u4 slot[16];
-  u2 sc[4];
+  u2 sc[4], zc[4];
   auto w_ptr = [&](const Item& it, int t, int s4) __attribute__((always_inline)) {
     const ProdRec& pr = rec[it.pi];
     const int32_t row = min(it.b0 + (wv + 8 * t) * 16 + 4 * s4 + (lane >> 4), it.b1 - 1);
@@ -182,6 +191,11 @@ __device__ __forceinline__ void run_msegment(const StreamPhase& seg, const Strea
     const ProdRec& pr = rec[it.pi];
     const int32_t row = min(it.b0 + (wv + 8 * t) * 16 + n16, it.b1 - 1);
     return reinterpret_cast<const u2*>(pr.sbase + (int64_t)row * GS + 4 * it.c);
+  };
+  auto z_ptr = [&](const Item& it, int t) __attribute__((always_inline)) {
+    const ProdRec& pr = rec[it.pi];
+    const int32_t row = min(it.b0 + (wv + 8 * t) * 16 + n16, it.b1 - 1);
+    return reinterpret_cast<const u2*>(pr.zbase + (int64_t)row * GS + 4 * it.c);
   };
 
   // ---- activations of one item: MT*16 rows x 512 k, PPT pieces per thread
@@ -217,11 +231,17 @@ __device__ __forceinline__ void run_msegment(const StreamPhase& seg, const Strea
       const float so = x_bits_to_float<XT>((uint16_t)(a0 >> 16)) + x_bits_to_float<XT>((uint16_t)(a1 >> 16)) +
                        x_bits_to_float<XT>((uint16_t)(a2 >> 16)) + x_bits_to_float<XT>((uint16_t)(a3 >> 16));
       float corr = D::BE * se + D::BO * so;
+      float sum = se + so;
       // the 16 pieces of one (row, group) are 16 aligned consecutive threads
 #pragma unroll
-      for (int o = 1; o < 16; o <<= 1) corr += __shfl_xor(corr, o, 64);
-      if ((k8 & 15) == 0)
+      for (int o = 1; o < 16; o <<= 1) {
+        corr += __shfl_xor(corr, o, 64);
+        if constexpr (ASYM) sum += __shfl_xor(sum, o, 64);
+      }
+      if ((k8 & 15) == 0) {
         *reinterpret_cast<float*>(buf + MT * 16384 + ((gs * MT + mt) * 16 + m16) * 4) = -corr;
+        if constexpr (ASYM) *reinterpret_cast<float*>(buf + MT * 16640 + ((gs * MT + mt) * 16 + m16) * 4) = sum;
+      }
     }
   };
 
@@ -273,13 +293,15 @@ __device__ __forceinline__ void run_msegment(const StreamPhase& seg, const Strea
 #pragma unroll
     for (int gs = 0; gs < 4; ++gs) {
       u4 a[MT][4];
-      f4 cneg[MT];
+      f4 cneg[MT], xsum[MT];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
         for (int d = 0; d < 4; ++d)
           a[mt][d] = *reinterpret_cast<const u4*>(buf + ((((gs * MT + mt) * 4 + d) * 4 + g) * 16 + n16) * 16);
         cneg[mt] = *reinterpret_cast<const f4*>(buf + MT * 16384 + ((gs * MT + mt) * 16 + 4 * g) * 4);
+        if constexpr (ASYM)
+          xsum[mt] = *reinterpret_cast<const f4*>(buf + MT * 16640 + ((gs * MT + mt) * 16 + 4 * g) * 4);
       }
 #pragma unroll
       for (int t = 0; t < MS_TW; ++t) {
@@ -290,10 +312,14 @@ __device__ __forceinline__ void run_msegment(const StreamPhase& seg, const Strea
           u4 bw[4];
 #pragma unroll
           for (int d = 0; d < 4; ++d) bw[d] = D::decode(wq[d]);
-          float s = 1.f;
+          float s = 1.f, z = 0.f;
           if constexpr (GROUPED) {
             const uint32_t sw = sc[2 * H + t][gs >> 1];
             s = f16_bits_to_float((uint16_t)((gs & 1) ? (sw >> 16) : (sw & 0xFFFFu)));
+          }
+          if constexpr (ASYM) {
+            const uint32_t zw = zc[2 * H + t][gs >> 1];
+            z = f16_bits_to_float((uint16_t)((gs & 1) ? (zw >> 16) : (zw & 0xFFFFu)));
           }
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
@@ -304,11 +330,14 @@ __device__ __forceinline__ void run_msegment(const StreamPhase& seg, const Strea
             for (int j = 0; j < 4; ++j) {
               if constexpr (GROUPED) acc[t][mt][j] = __builtin_fmaf(s, dd[j], acc[t][mt][j]);
               else acc[t][mt][j] += dd[j];
+              if constexpr (ASYM) acc[t][mt][j] = __builtin_fmaf(z, xsum[mt][j], acc[t][mt][j]);
             }
           }
         }
         if constexpr (GROUPED)
           if (gs == 3) sc[2 * H + t] = *to_global(s_ptr(pf, t));
+        if constexpr (ASYM)
+          if (gs == 3) zc[2 * H + t] = *to_global(z_ptr(pf, t));
       }
     }
     if (it.c == NC - 1) epilogue(it);
@@ -330,6 +359,10 @@ __device__ __forceinline__ void run_msegment(const StreamPhase& seg, const Strea
     if constexpr (GROUPED) {
       sc[t] = *to_global(s_ptr(cur, t));
       sc[2 + t] = *to_global(s_ptr(nx, t));
+    }
+    if constexpr (ASYM) {
+      zc[t] = *to_global(z_ptr(cur, t));
+      zc[2 + t] = *to_global(z_ptr(nx, t));
     }
   }
   if (sync) {
@@ -366,16 +399,20 @@ __device__ __forceinline__ void run_msegment(const StreamPhase& seg, const Strea
   __syncthreads();  // LDS is reused by the next segment
 }
 
-// variant = (x fp16 ? 0 : 2) + (grouped ? 1 : 0); 4 = a mix
-__host__ __device__ inline int mstream_variant(int xt, int group) { return (xt == XF16 ? 0 : 2) + (group ? 1 : 0); }
-constexpr int MVAR_ANY = 4;
+// variant = (x fp16 ? 0 : 3) + (asymmetric ? 2 : grouped ? 1 : 0); 6 = a mix
+__host__ __device__ inline int mstream_variant(int xt, int group, int asym) {
+  return (xt == XF16 ? 0 : 3) + (asym ? 2 : group ? 1 : 0);
+}
+constexpr int MVAR_ANY = 6;
 
 template <int MT, int V>
 __device__ __forceinline__ void mrun_variant(const StreamPhase& seg, const StreamProblem* probs,
                                              const StreamProblem& single, int2 wr, int m, uint8_t* smem,
                                              uint32_t* sync, uint32_t wt, bool coh) {
-  if (coh) run_msegment<V < 2 ? XF16 : XBF16, (V & 1) == 1, MT, true>(seg, probs, single, wr, m, smem, sync, wt);
-  else run_msegment<V < 2 ? XF16 : XBF16, (V & 1) == 1, MT, false>(seg, probs, single, wr, m, smem, sync, wt);
+  constexpr int XT = V < 3 ? XF16 : XBF16;
+  constexpr bool ASYM = V % 3 == 2, GROUPED = V % 3 != 0;
+  if (coh) run_msegment<XT, GROUPED, MT, true, ASYM>(seg, probs, single, wr, m, smem, sync, wt);
+  else run_msegment<XT, GROUPED, MT, false, ASYM>(seg, probs, single, wr, m, smem, sync, wt);
 }
 
 template <int MT, int VAR>
@@ -385,11 +422,13 @@ __device__ __forceinline__ void mseg_dispatch(const StreamPhase& seg, const Stre
   if constexpr (VAR != MVAR_ANY) {
     mrun_variant<MT, VAR>(seg, probs, single, wr, m, smem, sync, wt, coh);
   } else {
-    switch (mstream_variant(seg.xt, seg.group)) {
+    switch (mstream_variant(seg.xt, seg.group, seg.asym)) {
       case 0: mrun_variant<MT, 0>(seg, probs, single, wr, m, smem, sync, wt, coh); break;
       case 1: mrun_variant<MT, 1>(seg, probs, single, wr, m, smem, sync, wt, coh); break;
       case 2: mrun_variant<MT, 2>(seg, probs, single, wr, m, smem, sync, wt, coh); break;
-      default: mrun_variant<MT, 3>(seg, probs, single, wr, m, smem, sync, wt, coh); break;
+      case 3: mrun_variant<MT, 3>(seg, probs, single, wr, m, smem, sync, wt, coh); break;
+      case 4: mrun_variant<MT, 4>(seg, probs, single, wr, m, smem, sync, wt, coh); break;
+      default: mrun_variant<MT, 5>(seg, probs, single, wr, m, smem, sync, wt, coh); break;
     }
   }
 }
@@ -440,6 +479,8 @@ static const void* mstream_fn_var(int var) {
     case 1: return reinterpret_cast<const void*>(&gemm_mstream_kernel<MT, 1>);
     case 2: return reinterpret_cast<const void*>(&gemm_mstream_kernel<MT, 2>);
     case 3: return reinterpret_cast<const void*>(&gemm_mstream_kernel<MT, 3>);
+    case 4: return reinterpret_cast<const void*>(&gemm_mstream_kernel<MT, 4>);
+    case 5: return reinterpret_cast<const void*>(&gemm_mstream_kernel<MT, 5>);
     default: return reinterpret_cast<const void*>(&gemm_mstream_kernel<MT, MVAR_ANY>);
   }
 }
