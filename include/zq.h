@@ -198,13 +198,13 @@ zq_status zq_gemv(const zq_weight* W, const void* x, zq_dtype x_dtype, void* y,
  *           ZQ_F16 or ZQ_BF16.
  * Kernels by shape (all give results within the same tolerance of the exact
  * sums; integer-valued inputs give exact sums on every path). Asymmetric
- * weights run on the m <= 4 vector-ALU kernel or the general kernel:
+ * weights take the first three paths below, else the general kernel:
  *   m = 1, k a multiple of 128 (m <= 4 where the MFMA kernel below does
  *     not apply): a vector-ALU kernel that streams the codes once with
  *     128-bit loads;
  *   m = 2..32, INT4, k a multiple of 512, 16-byte aligned codes and
- *     activations, 8-byte aligned scales: a resident MFMA kernel that streams
- *     the codes once;
+ *     activations, 8-byte aligned scales (and zero points): a resident MFMA
+ *     kernel that streams the codes once;
  *   m > 32, INT4 with group scales (per-tensor scales: m <= 64), k a
  *     multiple of 512, aligned as above: that kernel on chunks of 32 rows;
  *   m > 64, one scale per tensor, k a multiple of 64: a tiled MFMA kernel
