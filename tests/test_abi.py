@@ -143,3 +143,35 @@ def test_asymmetric_weight_validation(L):
         w.zeros = 0x7000
         assert L.zq_unpack(ctypes.byref(w), 0x3000, zq.F32, None) == zq.ERR_UNSUPPORTED
         assert gemm(L, w) == zq.ERR_UNSUPPORTED
+
+
+def problems(entries):
+    """zq_problem array from (weight, m-independent fields, phase) entries,
+    with bogus 256-byte aligned host addresses (never touched)"""
+    arr = (zq._Problem * len(entries))()
+    for i, (w, xdt, phase) in enumerate(entries):
+        arr[i] = zq._Problem(w, 0x100000 + 0x1000 * i, xdt, w.k, 0x200000 + 0x1000 * i, zq.F32, w.n, phase)
+    return arr
+
+
+PLAN_CASES = [
+    # m, entries, status, detail
+    (0, [(dict(), zq.F16, 0)], zq.ERR_UNSUPPORTED, "m >= 1"),
+    # prefill plans (m > 64, one scale per tensor): one phase, one x dtype
+    (128, [(dict(group=0), zq.BF16, 0), (dict(group=0), zq.BF16, 1)], zq.ERR_UNSUPPORTED, "one phase"),
+    (128, [(dict(group=0), zq.BF16, 0), (dict(group=0), zq.F16, 0)], zq.ERR_UNSUPPORTED, "one activation type"),
+    (128, [(dict(group=0, k=200), zq.BF16, 0)], zq.ERR_UNSUPPORTED, "multiple of 64"),
+    # mid-batch plans (m > 32 otherwise): INT4 with k a multiple of 512 only
+    (48, [(dict(bits=8), zq.F16, 0)], zq.ERR_UNSUPPORTED, "INT4"),
+    (100, [(dict(bits=4, k=384), zq.BF16, 0)], zq.ERR_UNSUPPORTED, "multiple of 512"),
+    (40, [(dict(bits=2), zq.BF16, 0)], zq.ERR_UNSUPPORTED, "INT4"),
+]
+
+
+@pytest.mark.parametrize("m,entries,status,detail", PLAN_CASES)
+def test_plan_validation_without_device(L, m, entries, status, detail):
+    arr = problems([(W(**kw, n=64) if "k" in kw else W(**kw, n=64, k=512), xdt, ph) for kw, xdt, ph in entries])
+    h = ctypes.c_void_p()
+    assert L.zq_plan_create(arr, len(entries), m, ctypes.byref(h)) == status
+    assert detail in L.zq_last_error().decode()
+    assert not h.value
