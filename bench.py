@@ -259,7 +259,13 @@ def cpu_baseline(stack: Stack, torch, synth, budget_s: float = 12.0):
         value, unit = flops / wall / 1e12, "TFLOP/s"
     else:
         value, unit = done_bytes / wall / 1e9, "GB/s"
-    return {"value": round(value, 4), "unit": unit, "cores": threads, "kind": "oracle",
+    cpu_model = ""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            cpu_model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
+    except OSError:
+        pass
+    return {"value": round(value, 4), "unit": unit, "cores": threads, "kind": "oracle", "cpu_model": cpu_model,
             "sample": f"first {used_layers} of {stack.layers} layers (all {per_layer} projections, "
                       f"m={xrows} of {stack.m}), {cpu_seconds:.1f} CPU-s over {wall:.2f} s wall"}
 

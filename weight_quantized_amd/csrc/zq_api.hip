@@ -353,6 +353,7 @@ struct zq_plan_s {
   bool mfma = false;   // the MFMA batched-decode kernel (m >= MSTREAM_MIN_M)
   int64_t m = 1;
   int variant = 0;  // the kernel variant of the plan's one format, or the mixed-format one
+  int grid = 0;     // workgroups of the launch (the ranges table has one entry per segment and workgroup)
   size_t lds = 0;
   // prefill plans (m > 64): one tile queue per bit width, run in turn
   bool prefill = false;
@@ -366,14 +367,17 @@ struct zq_plan_s {
 };
 
 namespace {
-// products of segment `sg` touched by workgroup w of G: rows [w*N/G, (w+1)*N/G)
+// products of segment `sg` touched by workgroup w of the launch's G: rows
+// [w*N/Gs, (w+1)*N/Gs) for the Gs = sg.grid (or G) workgroups that share the
+// segment, none for the others
 void seg_ranges(const zq::StreamPhase& sg, const std::vector<zq::StreamProblem>& probs, int G,
                 std::vector<int2>& out) {
   const int64_t N = sg.n_total;
+  const int Gs = sg.grid > 0 && sg.grid < G ? sg.grid : G;
   int lo = 0;
   for (int w = 0; w < G; ++w) {
-    const int64_t r0 = w * N / G, r1 = (w + 1) * N / G;
-    if (r1 == r0) {
+    const int64_t r0 = w * N / Gs, r1 = (w + 1) * N / Gs;
+    if (w >= Gs || r1 == r0) {
       out.push_back(make_int2(0, 0));
       continue;
     }
@@ -628,9 +632,17 @@ zq_status zq_plan_create(const zq_problem* problems, int count, int64_t m, zq_pl
     sg.count += 1;
     sg.n_total += q.w.n;
   }
+  // Workgroups: one per CU, fewer for plans whose largest segment is small.
   // Split segments whose workgroup ranges would stage too many activation
   // buffers for LDS: halve them (no wait between the halves) until they fit.
-  const int G = zq::stream_grid();
+  int G = zq::stream_grid();
+  if (!mfma) {
+    G = 1;
+    for (zq::StreamPhase& sg : segs) {
+      sg.grid = zq::stream_grid_for(sg.bits, m, sg.n_total, sg.k);
+      G = std::max(G, sg.grid);
+    }
+  }
   std::vector<zq::StreamPhase> fitted;
   std::vector<int2> ranges;
   size_t lds = 0;
@@ -646,6 +658,7 @@ zq_status zq_plan_create(const zq_problem* problems, int count, int64_t m, zq_pl
         off += probs[sg.first + i].n;
       }
       sg.n_total = off;
+      if (!mfma) sg.grid = zq::stream_grid_for(sg.bits, m, sg.n_total, sg.k);
       std::vector<int2> r;
       seg_ranges(sg, probs, G, r);
       int maxrec = 1;
@@ -679,6 +692,7 @@ zq_status zq_plan_create(const zq_problem* problems, int count, int64_t m, zq_pl
   plan->nseg = (int)fitted.size();
   plan->m = m;
   plan->lds = lds;
+  plan->grid = G;
   plan->variant = variant;
   for (const zq::StreamPhase& sg : fitted) plan->waits = plan->waits || sg.wait;
   plan->mfma = mfma;
@@ -725,7 +739,8 @@ zq_status zq_plan_run(zq_plan plan, void* stream) {
                      ? zq::launch_mstream_plan(plan->segs, plan->nseg, plan->probs, plan->ranges, plan->m,
                                                plan->variant, plan->lds, plan->sync, plan->waits, (hipStream_t)stream)
                      : zq::launch_stream_plan(plan->segs, plan->nseg, plan->probs, plan->ranges, plan->m,
-                                              plan->variant, plan->lds, plan->sync, plan->waits, (hipStream_t)stream);
+                                              plan->variant, plan->lds, plan->sync, plan->waits, plan->grid,
+                                              (hipStream_t)stream);
   return e == hipSuccess ? ok() : hip_fail(e, "plan launch");
 }
 

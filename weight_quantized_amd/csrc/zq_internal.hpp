@@ -50,10 +50,15 @@ struct StreamPhase {
   int32_t first, count;  // problems [first, first + count) of the problem table
   int64_t n_total, k;
   int32_t bits, group, xt, wait;
-  int32_t asym, pad;     // asym: unsigned codes with zero points
+  int32_t asym;          // unsigned codes with zero points
+  int32_t grid;          // decode kernel: workgroups that share the segment's rows (0: all)
 };
 constexpr size_t STREAM_LDS_MAX = 160 * 1024;
 int stream_grid();  // workgroups of a stream launch (one per CU)
+// workgroups for a segment of n rows: at most one per CU, and no more than
+// give each wave about one step of 4 rows x 256 bytes (small products are
+// latency-bound: fewer, fuller workgroups start sooner)
+int stream_grid_for(int bits, int64_t m, int64_t n, int64_t k);
 // persistent, balanced kernel (1 <= m <= 4, rows of whole 256-byte steps)
 bool stream_supported(int bits, int group, int64_t m, int64_t n, int64_t k);
 size_t stream_lds_bytes(int bits, int64_t m, int64_t k, int nrec);
@@ -65,7 +70,7 @@ hipError_t launch_stream_single(const StreamProblem& p, int64_t m, hipStream_t s
 // every segment, or STREAM_VAR_ANY for a mix; sync = 3 device words
 hipError_t launch_stream_plan(const StreamPhase* dev_segs, int nseg, const StreamProblem* dev_probs,
                               const int2* dev_ranges, int64_t m, int variant, size_t lds, uint32_t* sync,
-                              bool waits, hipStream_t stream);
+                              bool waits, int grid, hipStream_t stream);
 
 // persistent MFMA kernel for batched decode: INT4, 2 <= m <= 32, k a
 // multiple of 512, 16-byte aligned codes and activations, 8-byte aligned

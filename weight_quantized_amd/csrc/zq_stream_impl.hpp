@@ -208,7 +208,10 @@ __device__ __forceinline__ void run_segment(const StreamPhase& seg, const Stream
   // wave index as a scalar: the run bookkeeping below is wave-uniform and
   // then lives in SGPRs with scalar branches
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int G = gridDim.x;
+  // the segment's rows are split over its own number of workgroups (the
+  // launch may have more, for larger segments): the same split as a single
+  // call on the segment alone
+  const int G = seg.grid > 0 && seg.grid < (int)gridDim.x ? seg.grid : (int)gridDim.x;
   const int64_t N = seg.n_total, k = seg.k;
   const int32_t C = (int32_t)(k / WPC);
   const int32_t CB = (C + 15) / 16;     // column blocks (steps) per row
@@ -217,6 +220,7 @@ __device__ __forceinline__ void run_segment(const StreamPhase& seg, const Stream
   const int64_t rowbytes = (int64_t)C * 16;
   const int32_t GS = (int32_t)(k / 128);
   const int64_t w = blockIdx.x;
+  if (w >= G) return;  // uniform: the segment's rows go to fewer workgroups
   const int32_t r0 = (int32_t)(w * N / G), r1 = (int32_t)((w + 1) * N / G);
   const int32_t R = r1 - r0;
   if (R == 0) return;  // uniform: this workgroup has no rows in the segment
