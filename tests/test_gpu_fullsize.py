@@ -6,7 +6,8 @@ and activation rows are copied back and recomputed by the fp64 oracle.
     Qwen2.5-7B decode stack with asymmetric INT4 weights, plan
     one rank's share of the 7B decode stack under 4-way tensor parallelism, plan
     Qwen2.5-32B decode stack  (64 layers x 7, M = 1), plan
-    7B stack, M = 8 and 32 (bf16 x), plan (MFMA batched-decode kernel)
+    7B stack, M = 4, 8, 32 and 128 (bf16 x), plan (MFMA batched-decode kernel,
+    in 32-row chunks past 32)
     7B prefill stack (per-layer INT2/4/8, per-tensor scale, M = 2048, bf16 x),
     plan (tile queues) and graph over 4 streams
 """
@@ -131,8 +132,9 @@ def test_qwen32b_decode_plan(mods):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("m", [4, 8, 32])
+@pytest.mark.parametrize("m", [4, 8, 32, 128])
 def test_qwen7b_batch_plan(mods, m):
+    # m = 128: four 32-row chunks, each a plan launch over all 196 products
     bench, zq = mods
     stack = bench.Stack("qwen7b-batch", m, None, torch, zq, synth)
     run_step(bench, stack, "plan")
