@@ -85,23 +85,29 @@ __device__ __forceinline__ float p2_sum8(const u4& p, float acc) {
 // step kk takes codes 8kk .. 8kk+7 of them, decoded in pair order, which
 // matches activation piece kc = 4g + kk staged by p2_perm.
 //
-// bf16 INT2 / INT4: a pair (code i, code i + E/2) of a dword moves, by one
-// shift, to bits 0.. of each 16-bit half; there it is the low fraction bits
-// of the bf16 number 128, whose unit in the last place is 1: (t & M) | 0x4300
-// is the exact value 128 + u, u = q + 2^(b-1) the code with its sign bit
-// flipped. The flip folds into the masking, ((t ^ S) & M) | O ==
-// (t & M) ^ ((S & M) ^ O): a shift and one v_bitop3 per pair. BIAS =
-// 128 + 2^(b-1) is removed in the epilogue. fp16 activations keep the
-// decoder with the smaller offset 16 + u: with 1024 + u the fp32 sums of
-// long rows would carry ten more bits of offset.
+// bf16 INT4: a pair (code i, code i + 4) of a dword moves, by one shift (none
+// for i = 0), to bits 3:0 of each 16-bit half; there it is the low fraction
+// bits of the bf16 number 128, whose unit in the last place is 1:
+// (t & M) | 0x4300 is the exact value 128 + u, u = q + 8 the code with its
+// sign bit flipped. The flip folds into the masking, ((t ^ S) & M) | O ==
+// (t & M) ^ ((S & M) ^ O): one v_bitop3 per pair; BIAS = 136.
+// bf16 INT2: a pair (code i, code i + 8) moves to bits 3:2, fraction bits of
+// the bf16 number 32 with unit 1: 32 + u, u = q + 2, BIAS = 34, again one
+// v_bitop3 per pair and a shift for three of the four. (Bits 1:0 under 128
+// cost the same but carry a 4 times larger offset into the fp32 sums, which
+// for INT2's small weights came to a fifth of the tolerance at k = 18944;
+// bits 6:5 under 4 need a fourth shift, 4 % slower.)
+// BIAS is removed in the epilogue. fp16 activations keep the decoder with
+// the offset 16 + u: with 1024 + u the fp32 sums of long rows would carry ten
+// more bits of offset.
 // INT8 (256 code values do not fit a bf16 fraction): byte -> float -> the
 // upper 16 bits, exact; BIAS = 128.
 template <int XT, int BITS>
 struct P2Dec {
   static constexpr bool FAST = XT == XBF16 && BITS <= 4;
-  static constexpr float BIAS = FAST ? 128.f + (float)(1 << (BITS - 1)) : Decoder<XT, BITS>::BIAS;
-  static constexpr uint32_t M = BITS == 4 ? 0x000F000Fu : 0x00030003u;
-  static constexpr uint32_t K = (BITS == 4 ? 0x00080008u : 0x00020002u) ^ 0x43004300u;
+  static constexpr float BIAS = !FAST ? Decoder<XT, BITS>::BIAS : BITS == 4 ? 136.f : 34.f;
+  static constexpr uint32_t M = BITS == 4 ? 0x000F000Fu : 0x000C000Cu;
+  static constexpr uint32_t K = BITS == 4 ? 0x00080008u ^ 0x43004300u : 0x00080008u ^ 0x42004200u;
 
   static __device__ __forceinline__ u4 frag(const u4 (&c)[2], int kk) {
     using Dc = Decoder<XT, BITS>;
@@ -111,7 +117,7 @@ struct P2Dec {
       return u4{(v & M) ^ K, ((v >> 4) & M) ^ K, ((v >> 8) & M) ^ K, ((v >> 12) & M) ^ K};
     } else if constexpr (FAST) {
       const uint32_t v = c[0][kk >> 1] >> ((kk & 1) * 8);  // pairs 0..3 or 4..7
-      return u4{(v & M) ^ K, ((v >> 2) & M) ^ K, ((v >> 4) & M) ^ K, ((v >> 6) & M) ^ K};
+      return u4{((v << 2) & M) ^ K, (v & M) ^ K, ((v >> 2) & M) ^ K, ((v >> 4) & M) ^ K};
     } else if constexpr (BITS == 4) {
       const uint32_t v = c[0][kk] ^ S;
       return u4{Dc::template pair<0>(v), Dc::template pair<1>(v), Dc::template pair<2>(v), Dc::template pair<3>(v)};
