@@ -56,8 +56,16 @@ __device__ __forceinline__ int p2_off(int r, int kc) { return r * 128 + ((kc ^ (
 //   INT2: slot g = k 4g + [0,8,1,9,2,10,3,11]
 template <int BITS>
 __device__ __forceinline__ void p2_perm(const u4& p0, const u4& p1, u4& s0, u4& s1) {
-  auto lo_lo = [](uint32_t a, uint32_t b) { return (a & 0xFFFFu) | (b << 16); };
-  auto hi_hi = [](uint32_t a, uint32_t b) { return (a >> 16) | (b & 0xFFFF0000u); };
+  // INT8: one v_perm_b32 each (byte selectors: 0-3 pick bytes of a, 4-7 of
+  // b). INT2/INT4 keep shift-and-mask forms, which measured faster there.
+  auto lo_lo = [](uint32_t a, uint32_t b) {
+    if constexpr (BITS == 8) return __builtin_amdgcn_perm(b, a, 0x05040100u);
+    else return (a & 0xFFFFu) | (b << 16);
+  };
+  auto hi_hi = [](uint32_t a, uint32_t b) {
+    if constexpr (BITS == 8) return __builtin_amdgcn_perm(b, a, 0x07060302u);
+    else return (a >> 16) | (b & 0xFFFF0000u);
+  };
   if constexpr (BITS == 4) {
     s0 = u4{lo_lo(p0[0], p0[2]), hi_hi(p0[0], p0[2]), lo_lo(p0[1], p0[3]), hi_hi(p0[1], p0[3])};
     s1 = u4{lo_lo(p1[0], p1[2]), hi_hi(p1[0], p1[2]), lo_lo(p1[1], p1[3]), hi_hi(p1[1], p1[3])};
@@ -121,6 +129,15 @@ struct P2Dec {
     } else if constexpr (BITS == 4) {
       const uint32_t v = c[0][kk] ^ S;
       return u4{Dc::template pair<0>(v), Dc::template pair<1>(v), Dc::template pair<2>(v), Dc::template pair<3>(v)};
+    } else if constexpr (BITS == 8 && XT == XBF16) {
+      // bytes I and I + 2 of a dword -> exact floats -> their upper halves,
+      // joined by one v_perm_b32
+      const uint32_t v0 = c[kk >> 1][2 * (kk & 1)] ^ S, v1 = c[kk >> 1][2 * (kk & 1) + 1] ^ S;
+      auto pr = [](uint32_t v, int i) __attribute__((always_inline)) {
+        const float lo = (float)((v >> (8 * i)) & 0xFFu), hi = (float)((v >> (8 * (i + 2))) & 0xFFu);
+        return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+      };
+      return u4{pr(v0, 0), pr(v0, 1), pr(v1, 0), pr(v1, 1)};
     } else if constexpr (BITS == 8) {
       const uint32_t v0 = c[kk >> 1][2 * (kk & 1)] ^ S, v1 = c[kk >> 1][2 * (kk & 1) + 1] ^ S;
       return u4{Dc::template pair<0>(v0), Dc::template pair<1>(v0), Dc::template pair<0>(v1),

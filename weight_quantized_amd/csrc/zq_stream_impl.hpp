@@ -43,7 +43,10 @@
 
 namespace zq {
 
-constexpr int ST_U = 8;
+// chunks in flight per lane: 4 (64 KB per CU at 1024 threads) streamed the
+// 7B, 32B and tensor-parallel stacks 2-5 % faster than 8; 2 and 3 were no
+// better than 4
+constexpr int ST_U = 4;
 // 1024 threads (16 waves, 128 VGPRs) for one activation row; 512 threads
 // (256 VGPRs) when each lane keeps 2..4 rows of partials.
 template <int MR>
