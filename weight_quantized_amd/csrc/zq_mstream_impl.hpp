@@ -47,6 +47,9 @@ constexpr int MS_THREADS = 512;  // 8 waves
 constexpr int MS_KC = 512;       // k per chunk (4 groups of 128)
 constexpr int MS_TW = 2;         // 16-row tiles per wave per block
 constexpr int MS_BLOCK = 8 * MS_TW * 16;
+// items whose weights are in flight ahead of the one computed: 1 (64 KB per
+// CU) streamed 0.4-1 % faster than 2 at M = 2..64, with ~40 fewer VGPRs
+constexpr int MS_AHEAD = 1;
 
 // LDS bytes of one activation chunk buffer: A fragments [gs][mt][d][g][m][8]
 // (16 bytes each), the negated offset sums [gs][mt][m] (fp32) and, for
@@ -174,14 +177,15 @@ __device__ __forceinline__ void run_msegment(const StreamPhase& seg, const Strea
     return valid(nx) ? nx : it;
   };
 
-  // ---- weight stream: 16 register slots per lane, two items of this wave's
-  // two tiles; slot 8h + 4t + s holds rows 4s..4s+3 of tile t of an item of
-  // parity h (lane l: row 4s + l/16, bytes 16*(l%16) of the chunk). Slots
-  // are refilled with the item two ahead as soon as they are moved to LDS.
+  // ---- weight stream: 8 register slots per lane and item in flight, for
+  // this wave's two tiles; slot 8h + 4t + s holds rows 4s..4s+3 of tile t of
+  // an item (of parity h when two are in flight; lane l: row 4s + l/16, bytes
+  // 16*(l%16) of the chunk). Slots are refilled with the item MS_AHEAD ahead
+  // as soon as they are moved to LDS.
   // Loads are unconditional (tiles past a block's end re-read its last row),
   // so the compiler counts them exactly.
-  u4 slot[16];
-  u2 sc[4], zc[4];
+  u4 slot[8 * MS_AHEAD];
+  u2 sc[2 * MS_AHEAD], zc[2 * MS_AHEAD];
   auto w_ptr = [&](const Item& it, int t, int s4) __attribute__((always_inline)) {
     const ProdRec& pr = rec[it.pi];
     const int32_t row = min(it.b0 + (wv + 8 * t) * 16 + 4 * s4 + (lane >> 4), it.b1 - 1);
@@ -270,12 +274,14 @@ __device__ __forceinline__ void run_msegment(const StreamPhase& seg, const Strea
     }
   };
 
-  // One item of parity H: x for it is in LDS buffer H; the slots 8H.. hold
-  // its weights. Loads the next item's activations and refills the slots
-  // with item `pf` (two ahead), then stages the activations and waits for
-  // the workgroup.
-  auto process = [&]<int H>(const Item& it, const Item& nx, const Item& pf) __attribute__((always_inline)) {
+  // One item of parity H: x for it is in LDS buffer H; the slots hold its
+  // weights. Loads the next item's activations and refills the slots with
+  // the item MS_AHEAD ahead (`nx`, or `pf2` two ahead), then stages the
+  // activations and waits for the workgroup.
+  auto process = [&]<int H>(const Item& it, const Item& nx, const Item& pf2) __attribute__((always_inline)) {
     const uint8_t* buf = xbuf + H * XB;
+    constexpr int SB = MS_AHEAD == 2 ? 8 * H : 0, CB2 = MS_AHEAD == 2 ? 2 * H : 0;
+    const Item& pf = MS_AHEAD == 2 ? pf2 : nx;
     load_x(nx);
     // this item's weights -> the wave's scratch; refill the slots at once
 #pragma unroll
@@ -283,12 +289,12 @@ __device__ __forceinline__ void run_msegment(const StreamPhase& seg, const Strea
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4)
         *reinterpret_cast<u4*>(wscr + t * MS_TTILE + s4 * MS_TLOAD + (lane >> 4) * MS_TROW + (lane & 15) * 16) =
-            slot[8 * H + 4 * t + s4];
+            slot[SB + 4 * t + s4];
 #pragma unroll
     for (int t = 0; t < MS_TW; ++t)
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4)
-        slot[8 * H + 4 * t + s4] = __builtin_nontemporal_load(to_global(w_ptr(pf, t, s4)));
+        slot[SB + 4 * t + s4] = __builtin_nontemporal_load(to_global(w_ptr(pf, t, s4)));
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int gs = 0; gs < 4; ++gs) {
@@ -314,11 +320,11 @@ __device__ __forceinline__ void run_msegment(const StreamPhase& seg, const Strea
           for (int d = 0; d < 4; ++d) bw[d] = D::decode(wq[d]);
           float s = 1.f, z = 0.f;
           if constexpr (GROUPED) {
-            const uint32_t sw = sc[2 * H + t][gs >> 1];
+            const uint32_t sw = sc[CB2 + t][gs >> 1];
             s = f16_bits_to_float((uint16_t)((gs & 1) ? (sw >> 16) : (sw & 0xFFFFu)));
           }
           if constexpr (ASYM) {
-            const uint32_t zw = zc[2 * H + t][gs >> 1];
+            const uint32_t zw = zc[CB2 + t][gs >> 1];
             z = f16_bits_to_float((uint16_t)((gs & 1) ? (zw >> 16) : (zw & 0xFFFFu)));
           }
 #pragma unroll
@@ -335,9 +341,9 @@ __device__ __forceinline__ void run_msegment(const StreamPhase& seg, const Strea
           }
         }
         if constexpr (GROUPED)
-          if (gs == 3) sc[2 * H + t] = *to_global(s_ptr(pf, t));
+          if (gs == 3) sc[CB2 + t] = *to_global(s_ptr(pf, t));
         if constexpr (ASYM)
-          if (gs == 3) zc[2 * H + t] = *to_global(z_ptr(pf, t));
+          if (gs == 3) zc[CB2 + t] = *to_global(z_ptr(pf, t));
       }
     }
     if (it.c == NC - 1) epilogue(it);
@@ -345,7 +351,7 @@ __device__ __forceinline__ void run_msegment(const StreamPhase& seg, const Strea
     __syncthreads();  // also orders this wave's scratch reads before the next item's writes
   };
 
-  // ---- prologue: the first two items' weights (they do not depend on
+  // ---- prologue: the first MS_AHEAD items' weights (they do not depend on
   // earlier phases), then the phase wait, then the first activations
   Item cur = first_item();
   Item nx = next_or_same(cur);
@@ -354,15 +360,15 @@ __device__ __forceinline__ void run_msegment(const StreamPhase& seg, const Strea
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
       slot[4 * t + s4] = __builtin_nontemporal_load(to_global(w_ptr(cur, t, s4)));
-      slot[8 + 4 * t + s4] = __builtin_nontemporal_load(to_global(w_ptr(nx, t, s4)));
+      if constexpr (MS_AHEAD == 2) slot[(MS_AHEAD - 1) * 8 + 4 * t + s4] = __builtin_nontemporal_load(to_global(w_ptr(nx, t, s4)));
     }
     if constexpr (GROUPED) {
       sc[t] = *to_global(s_ptr(cur, t));
-      sc[2 + t] = *to_global(s_ptr(nx, t));
+      if constexpr (MS_AHEAD == 2) sc[(MS_AHEAD - 1) * 2 + t] = *to_global(s_ptr(nx, t));
     }
     if constexpr (ASYM) {
       zc[t] = *to_global(z_ptr(cur, t));
-      zc[2 + t] = *to_global(z_ptr(nx, t));
+      if constexpr (MS_AHEAD == 2) zc[(MS_AHEAD - 1) * 2 + t] = *to_global(z_ptr(nx, t));
     }
   }
   if (sync) {
