@@ -54,7 +54,7 @@ hipError_t launch_mstream_single(const StreamProblem& p, int64_t m, hipStream_t 
   uint32_t* nosync = nullptr;
   int mi = (int)m;
   void* args[] = {&none, &nseg, &noprobs, &noranges, &seg, &pp, &nosync, &mi};
-  return hipLaunchKernel(fn, dim3(grid), dim3(MS_THREADS), args, lds, stream);
+  return hipLaunchKernel(fn, dim3(grid), dim3(m <= 16 ? ms_threads<1>() : ms_threads<2>()), args, lds, stream);
 }
 
 hipError_t launch_mstream_plan(const StreamPhase* dev_segs, int nseg, const StreamProblem* dev_probs,
@@ -67,7 +67,7 @@ hipError_t launch_mstream_plan(const StreamPhase* dev_segs, int nseg, const Stre
   StreamProblem dpr{};
   int mi = (int)m;
   void* args[] = {(void*)&dev_segs, &nseg, (void*)&dev_probs, (void*)&dev_ranges, &dseg, &dpr, &sync, &mi};
-  const dim3 grid(stream_grid()), block(MS_THREADS);
+  const dim3 grid(stream_grid()), block(m <= 16 ? ms_threads<1>() : ms_threads<2>());
   if (waits) return hipLaunchCooperativeKernel(fn, grid, block, args, (unsigned)lds, stream);
   return hipLaunchKernel(fn, grid, block, args, lds, stream);
 }

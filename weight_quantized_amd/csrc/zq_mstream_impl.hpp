@@ -31,9 +31,10 @@
 //     group, is staged with the activations and enters the first MFMA of the
 //     group as its C operand, negated, so the MFMA output is the group's
 //     exact-input dot product;
-//   * a workgroup (8 waves) owns a contiguous range of the segment's row
-//     space; it walks it in blocks of up to 256 rows inside one product
-//     (wave w takes the 16-row tiles w and w + 8) and each block in chunks
+//   * a workgroup (16 waves for up to 16 activation rows, 8 for more) owns
+//     a contiguous range of the segment's row space; it walks it in blocks
+//     of up to 256 rows inside one product (wave w takes 16-row tile w, or
+//     tiles w and w + 8 with 8 waves) and each block in chunks
 //     of 512 k: activations of the next chunk are loaded into registers and
 //     the weights of the next chunk are in flight while the current chunk is
 //     computed; the activation buffers in LDS are double buffered;
@@ -43,10 +44,19 @@
 
 namespace zq {
 
-constexpr int MS_THREADS = 512;  // 8 waves
+// One 16-row activation tile (M <= 16): 16 waves with one 16-row weight
+// tile each per block; two (M = 17..32): 8 waves with two each, since the
+// second tile's accumulators and fragments do not fit 128 VGPRs. Both walk
+// 256-row blocks and use the same transpose scratch. At M = 2..16 the 16
+// waves streamed 11-23 % faster than 8.
+template <int MT>
+__host__ __device__ constexpr int ms_threads() { return MT == 1 ? 1024 : 512; }
+template <int MT>
+__host__ __device__ constexpr int ms_tw() { return MT == 1 ? 1 : 2; }  // 16-row tiles per wave per block
 constexpr int MS_KC = 512;       // k per chunk (4 groups of 128)
-constexpr int MS_TW = 2;         // 16-row tiles per wave per block
-constexpr int MS_BLOCK = 8 * MS_TW * 16;
+constexpr int MS_BLOCK = 256;  // rows per block: waves x tiles per wave x 16
+static_assert(ms_threads<1>() / 64 * ms_tw<1>() * 16 == MS_BLOCK && ms_threads<2>() / 64 * ms_tw<2>() * 16 == MS_BLOCK,
+              "both tile counts walk the same blocks");
 // items whose weights are in flight ahead of the one computed: 1 (64 KB per
 // CU) streamed 0.4-1 % faster than 2 at M = 2..64, with ~40 fewer VGPRs
 constexpr int MS_AHEAD = 1;
@@ -59,10 +69,10 @@ __host__ __device__ constexpr int mstream_xbuf_bytes(int mt) { return mt * (4 * 
 // pieces of 16 bytes, each 16-piece row padded by 16 bytes (272 bytes) so
 // that both the row-wise writes and the tile-column reads are conflict-free.
 constexpr int MS_TROW = 272, MS_TLOAD = 4 * MS_TROW, MS_TTILE = 4 * MS_TLOAD;
-constexpr int MS_WSCR = MS_TW * MS_TTILE;
+constexpr int MS_WSCR_ALL = (MS_BLOCK / 16) * MS_TTILE;  // all waves' scratch of one workgroup
 
 __host__ __device__ inline size_t mstream_lds_bytes(int mt, int nrec) {
-  return (size_t)nrec * PROD_REC_BYTES + 2 * (size_t)mstream_xbuf_bytes(mt) + 8 * (size_t)MS_WSCR;
+  return (size_t)nrec * PROD_REC_BYTES + 2 * (size_t)mstream_xbuf_bytes(mt) + (size_t)MS_WSCR_ALL;
 }
 
 // INT4 decoder for the MFMA kernel: raw packed dword -> 4 dwords of packed
@@ -121,7 +131,9 @@ __device__ __forceinline__ void run_msegment(const StreamPhase& seg, const Strea
   static_assert(!ASYM || GROUPED, "zero points come per 128-group");
   constexpr bool coherent = COH;
   using D = MDec<XT, ASYM>;
-  constexpr int NT = MS_THREADS;
+  constexpr int NT = ms_threads<MT>();
+  constexpr int NWV = NT / 64;  // waves
+  constexpr int TW = ms_tw<MT>();
   constexpr int XB = mstream_xbuf_bytes(MT);
   constexpr int PPT = MT * 16 * 64 / NT;  // activation pieces (8 values) per thread per chunk
 
@@ -142,7 +154,7 @@ __device__ __forceinline__ void run_msegment(const StreamPhase& seg, const Strea
 
   ProdRec* rec = reinterpret_cast<ProdRec*>(smem);
   uint8_t* xbuf = smem + (size_t)nrec * sizeof(ProdRec);
-  uint8_t* wscr = xbuf + 2 * XB + wv * MS_WSCR;  // this wave's transpose scratch
+  uint8_t* wscr = xbuf + 2 * XB + wv * TW * MS_TTILE;  // this wave's transpose scratch
   for (int i = tid; i < nrec; i += NT) {
     const StreamProblem& p = probs ? probs[seg.first + wr.x + i] : single;
     rec[i] = make_rec(p, rowbytes, GS, GROUPED);
@@ -177,28 +189,28 @@ __device__ __forceinline__ void run_msegment(const StreamPhase& seg, const Strea
     return valid(nx) ? nx : it;
   };
 
-  // ---- weight stream: 8 register slots per lane and item in flight, for
-  // this wave's two tiles; slot 8h + 4t + s holds rows 4s..4s+3 of tile t of
-  // an item (of parity h when two are in flight; lane l: row 4s + l/16, bytes
-  // 16*(l%16) of the chunk). Slots are refilled with the item MS_AHEAD ahead
-  // as soon as they are moved to LDS.
+  // ---- weight stream: 4 register slots per lane, tile and item in flight,
+  // for this wave's TW tiles; slot 4TWh + 4t + s holds rows 4s..4s+3 of tile
+  // t of an item (of parity h when two are in flight; lane l: row 4s + l/16,
+  // bytes 16*(l%16) of the chunk). Slots are refilled with the item MS_AHEAD
+  // ahead as soon as they are moved to LDS.
   // Loads are unconditional (tiles past a block's end re-read its last row),
   // so the compiler counts them exactly.
-  u4 slot[8 * MS_AHEAD];
-  u2 sc[2 * MS_AHEAD], zc[2 * MS_AHEAD];
+  u4 slot[4 * TW * MS_AHEAD];
+  u2 sc[TW * MS_AHEAD], zc[TW * MS_AHEAD];
   auto w_ptr = [&](const Item& it, int t, int s4) __attribute__((always_inline)) {
     const ProdRec& pr = rec[it.pi];
-    const int32_t row = min(it.b0 + (wv + 8 * t) * 16 + 4 * s4 + (lane >> 4), it.b1 - 1);
+    const int32_t row = min(it.b0 + (wv + NWV * t) * 16 + 4 * s4 + (lane >> 4), it.b1 - 1);
     return reinterpret_cast<const u4*>(pr.wbase + (int64_t)row * rowbytes + (int64_t)it.c * 256) + (lane & 15);
   };
   auto s_ptr = [&](const Item& it, int t) __attribute__((always_inline)) {
     const ProdRec& pr = rec[it.pi];
-    const int32_t row = min(it.b0 + (wv + 8 * t) * 16 + n16, it.b1 - 1);
+    const int32_t row = min(it.b0 + (wv + NWV * t) * 16 + n16, it.b1 - 1);
     return reinterpret_cast<const u2*>(pr.sbase + (int64_t)row * GS + 4 * it.c);
   };
   auto z_ptr = [&](const Item& it, int t) __attribute__((always_inline)) {
     const ProdRec& pr = rec[it.pi];
-    const int32_t row = min(it.b0 + (wv + 8 * t) * 16 + n16, it.b1 - 1);
+    const int32_t row = min(it.b0 + (wv + NWV * t) * 16 + n16, it.b1 - 1);
     return reinterpret_cast<const u2*>(pr.zbase + (int64_t)row * GS + 4 * it.c);
   };
 
@@ -249,17 +261,17 @@ __device__ __forceinline__ void run_msegment(const StreamPhase& seg, const Strea
     }
   };
 
-  f4 acc[MS_TW][MT];
+  f4 acc[TW][MT];
 #pragma unroll
-  for (int t = 0; t < MS_TW; ++t)
+  for (int t = 0; t < TW; ++t)
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f4{0.f, 0.f, 0.f, 0.f};
 
   auto epilogue = [&](const Item& it) __attribute__((always_inline)) {
     const ProdRec& pr = rec[it.pi];
 #pragma unroll
-    for (int t = 0; t < MS_TW; ++t) {
-      const int32_t row = it.b0 + (wv + 8 * t) * 16 + n16;
+    for (int t = 0; t < TW; ++t) {
+      const int32_t row = it.b0 + (wv + NWV * t) * 16 + n16;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
@@ -280,18 +292,18 @@ __device__ __forceinline__ void run_msegment(const StreamPhase& seg, const Strea
   // activations and waits for the workgroup.
   auto process = [&]<int H>(const Item& it, const Item& nx, const Item& pf2) __attribute__((always_inline)) {
     const uint8_t* buf = xbuf + H * XB;
-    constexpr int SB = MS_AHEAD == 2 ? 8 * H : 0, CB2 = MS_AHEAD == 2 ? 2 * H : 0;
+    constexpr int SB = MS_AHEAD == 2 ? 4 * TW * H : 0, CB2 = MS_AHEAD == 2 ? TW * H : 0;
     const Item& pf = MS_AHEAD == 2 ? pf2 : nx;
     load_x(nx);
     // this item's weights -> the wave's scratch; refill the slots at once
 #pragma unroll
-    for (int t = 0; t < MS_TW; ++t)
+    for (int t = 0; t < TW; ++t)
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4)
         *reinterpret_cast<u4*>(wscr + t * MS_TTILE + s4 * MS_TLOAD + (lane >> 4) * MS_TROW + (lane & 15) * 16) =
             slot[SB + 4 * t + s4];
 #pragma unroll
-    for (int t = 0; t < MS_TW; ++t)
+    for (int t = 0; t < TW; ++t)
 #pragma unroll
       for (int s4 = 0; s4 < 4; ++s4)
         slot[SB + 4 * t + s4] = __builtin_nontemporal_load(to_global(w_ptr(pf, t, s4)));
@@ -310,11 +322,11 @@ __device__ __forceinline__ void run_msegment(const StreamPhase& seg, const Strea
           xsum[mt] = *reinterpret_cast<const f4*>(buf + MT * 16640 + ((gs * MT + mt) * 16 + 4 * g) * 4);
       }
 #pragma unroll
-      for (int t = 0; t < MS_TW; ++t) {
+      for (int t = 0; t < TW; ++t) {
         // row n16 of the tile, bytes 64 gs + 16 g: load n16/4, row n16%4, piece 4 gs + g
         const u4 wq = *reinterpret_cast<const u4*>(wscr + t * MS_TTILE + (n16 >> 2) * MS_TLOAD +
                                                    (n16 & 3) * MS_TROW + (4 * gs + g) * 16);
-        if (it.b0 + (wv + 8 * t) * 16 < it.b1) {  // wave-uniform: the tile has rows
+        if (it.b0 + (wv + NWV * t) * 16 < it.b1) {  // wave-uniform: the tile has rows
           u4 bw[4];
 #pragma unroll
           for (int d = 0; d < 4; ++d) bw[d] = D::decode(wq[d]);
@@ -356,19 +368,19 @@ __device__ __forceinline__ void run_msegment(const StreamPhase& seg, const Strea
   Item cur = first_item();
   Item nx = next_or_same(cur);
 #pragma unroll
-  for (int t = 0; t < MS_TW; ++t) {
+  for (int t = 0; t < TW; ++t) {
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4) {
       slot[4 * t + s4] = __builtin_nontemporal_load(to_global(w_ptr(cur, t, s4)));
-      if constexpr (MS_AHEAD == 2) slot[(MS_AHEAD - 1) * 8 + 4 * t + s4] = __builtin_nontemporal_load(to_global(w_ptr(nx, t, s4)));
+      if constexpr (MS_AHEAD == 2) slot[(MS_AHEAD - 1) * 4 * TW + 4 * t + s4] = __builtin_nontemporal_load(to_global(w_ptr(nx, t, s4)));
     }
     if constexpr (GROUPED) {
       sc[t] = *to_global(s_ptr(cur, t));
-      if constexpr (MS_AHEAD == 2) sc[(MS_AHEAD - 1) * 2 + t] = *to_global(s_ptr(nx, t));
+      if constexpr (MS_AHEAD == 2) sc[(MS_AHEAD - 1) * TW + t] = *to_global(s_ptr(nx, t));
     }
     if constexpr (ASYM) {
       zc[t] = *to_global(z_ptr(cur, t));
-      if constexpr (MS_AHEAD == 2) zc[(MS_AHEAD - 1) * 2 + t] = *to_global(z_ptr(nx, t));
+      if constexpr (MS_AHEAD == 2) zc[(MS_AHEAD - 1) * TW + t] = *to_global(z_ptr(nx, t));
     }
   }
   if (sync) {
@@ -441,7 +453,7 @@ __device__ __forceinline__ void mseg_dispatch(const StreamPhase& seg, const Stre
 
 // Same launch contract as gemv_stream_kernel, plus the activation row count.
 template <int MT, int VAR>
-__global__ __launch_bounds__(MS_THREADS) void gemm_mstream_kernel(
+__global__ __launch_bounds__(ms_threads<MT>()) void gemm_mstream_kernel(
     const StreamPhase* __restrict__ segs, int nseg, const StreamProblem* __restrict__ probs,
     const int2* __restrict__ wranges, StreamPhase single_seg, StreamProblem single_prob, uint32_t* sync, int m) {
   extern __shared__ __align__(16) uint8_t smem[];
