@@ -54,7 +54,7 @@ def check(y, yref, x, xdt, q, group, s, what=""):
 
 @pytest.mark.parametrize("xdt", ["f16", "bf16"])
 @pytest.mark.parametrize("group", [0, 128])
-@pytest.mark.parametrize("m", [5, 8, 13, 16, 17, 24, 32])
+@pytest.mark.parametrize("m", [2, 3, 4, 5, 8, 13, 16, 17, 24, 32])
 def test_mstream_gemm_matches_oracle(xdt, group, m):
     # ragged tiles (300 = 18 x 16 + 12), several 256-row blocks, 1 and 3 chunks
     for n, k in [(16, 512), (300, 1536), (1000, 512)]:
@@ -94,7 +94,7 @@ def test_mstream_long_k_and_low_precision_out():
     assert torch.equal(Yh, Y.to(torch.bfloat16))  # same sums, rounded once
 
 
-@pytest.mark.parametrize("m", [8, 32])
+@pytest.mark.parametrize("m", [2, 8, 16, 17, 32])
 def test_mstream_plan_matches_oracle_and_single_calls(m):
     spec = [(128, 512, 1024, "f16", 0), (0, 300, 1024, "f16", 0), (128, 4096, 512, "bf16", 1),
             (0, 640, 2048, "bf16", 1), (128, 3584, 3584, "f16", 2)]
