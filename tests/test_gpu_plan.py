@@ -169,3 +169,77 @@ def test_plan_m4_long_k(xdt):
         tol = 2e-3 * xn * np.abs(O.dequant(q, 128, s)).max(1)[None, :] + 1e-3 * np.abs(yref)
         assert np.all(np.abs(Y.double().cpu().numpy() - yref) <= tol)
         assert torch.equal(zq.gemm(W, X), Y)
+
+
+def _check_chain(plan, y0, x0h, W0ref, later, xdt, runs=3):
+    """run `plan` `runs` times with y0 (phase 0's output, the later phase's
+    input) NaN-filled before each run; check phase 0 against the oracle and
+    each later product against the oracle on the y0 values actually stored"""
+    q0, s0, p0, g0, b0, n0, k0 = W0ref
+    for _ in range(runs):
+        y0.fill_(float("nan"))
+        for _, _, Y, _ in later:
+            Y.fill_(float("nan"))
+        plan.run()
+        torch.cuda.synchronize()
+        plan.check()
+        y0_host = y0.cpu()
+        assert not torch.isnan(y0_host).any()
+        y0ref = O.gemm(p0, b0, s0, g0, n0, k0, x0h, xdt)
+        y0bits = y0_host.view(torch.int16).numpy().view(np.uint16) if xdt == "bf16" else y0_host.numpy()
+        y0_64 = x64(y0bits, xdt)
+        xn = np.sqrt((x64(x0h, xdt) ** 2).sum(1))[:, None]
+        tol0 = 2e-3 * xn * np.abs(O.dequant(q0, g0, s0)).max(1)[None, :] + 1e-3 * np.abs(y0ref)
+        tol0 = tol0 + 0.5 * np.abs(y0ref) * (2.0 ** -7 if xdt == "bf16" else 2.0 ** -10)
+        assert np.all(np.abs(y0_64 - y0ref) <= tol0)
+        xn1 = np.sqrt((y0_64 ** 2).sum(1))[:, None]
+        for W, _, Y, (q, s, p, bits, group, n, k) in later:
+            y = Y.double().cpu().numpy()
+            assert not np.isnan(y).any(), "a later segment read the earlier phase's output before it was stored"
+            yref = O.gemm(p, bits, s, group, n, k, y0bits, xdt)
+            tol = 2e-3 * xn1 * np.abs(O.dequant(q, group, s)).max(1)[None, :] + 1e-3 * np.abs(yref)
+            assert np.all(np.abs(y - yref) <= tol)
+
+
+def _chain_plan(m, xdt, first, later_specs, seed):
+    """phase 0: y0 = W0 x0 (y0 in the activation dtype); phase 1: the products
+    of later_specs (bits, group, n) all read y0"""
+    b0, g0, n0, k0 = first
+    q0, s0, p0, W0 = weight(b0, g0, n0, k0, seed=seed)
+    x0h = synth.normal(synth.rng(seed + 1), (m, k0), xdt)
+    tdt = torch.bfloat16 if xdt == "bf16" else torch.float16
+    y0 = torch.empty((m, n0), dtype=tdt, device=DEV)
+    probs = [(W0, x_dev(x0h, xdt), y0, 0)]
+    later = []
+    for i, (bits, group, n) in enumerate(later_specs):
+        q, s, p, W = weight(bits, group, n, n0, seed=seed + 10 + i)
+        Y = torch.empty((m, n), dtype=torch.float32, device=DEV)
+        probs.append((W, y0, Y, 1))
+        later.append((W, y0, Y, (q, s, p, bits, group, n, n0)))
+    return zq.Plan(probs), y0, x0h, (q0, s0, p0, g0, b0, n0, k0), later
+
+
+def test_phase_wait_when_first_segment_has_fewer_workgroups():
+    """vector-ALU plan, m = 1. Phase 0 (16 workgroups) writes y0; phase 1 is an
+    INT2 segment spread over 1 workgroup, then an INT4 segment over 256: the
+    workgroups with no INT2 rows must still wait before they read y0."""
+    plan, y0, x0h, ref0, later = _chain_plan(1, "f16", (4, 128, 1024, 256), [(2, 128, 16), (4, 128, 8192)], 700)
+    _check_chain(plan, y0, x0h, ref0, later, "f16")
+
+
+def test_phase_wait_across_lds_split_segments():
+    """vector-ALU plan, m = 4. Phase 1 holds 40 one-row INT2 products and one
+    of 2048 rows, all of k = 128: a workgroup's range would stage more
+    activation buffers than LDS holds, so the phase is cut into segments of
+    10, 10, 10 and 11 products without waits between them; only the last one
+    spreads over more than one workgroup."""
+    specs = [(2, 128, 1)] * 40 + [(2, 128, 2048)]
+    plan, y0, x0h, ref0, later = _chain_plan(4, "f16", (4, 128, 128, 256), specs, 800)
+    _check_chain(plan, y0, x0h, ref0, later, "f16")
+
+
+def test_mstream_phase_wait_when_first_segment_has_few_rows():
+    """MFMA batched-decode plan, m = 8: phase 1 is a per-tensor INT4 segment of
+    16 rows (rows on 16 of 256 workgroups), then a group-scaled one of 8192."""
+    plan, y0, x0h, ref0, later = _chain_plan(8, "bf16", (4, 128, 1024, 18944), [(4, 0, 16), (4, 128, 8192)], 900)
+    _check_chain(plan, y0, x0h, ref0, later, "bf16")

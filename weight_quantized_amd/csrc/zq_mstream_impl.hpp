@@ -119,13 +119,15 @@ __device__ __forceinline__ f4 ms_mfma(u4 a, u4 b, f4 c) {
 
 // seg: segment; probs: problem table (nullptr: `single`); wr: {first, last}
 // problem of the segment touched by this workgroup; m: activation rows
-// (<= 16 * MT).
+// (<= 16 * MT); sync (non-null): a phase wait not performed yet by this
+// workgroup. Returns false when the workgroup has no rows in the segment (it
+// then read nothing and the wait stays pending for its next segment).
 // COH: activations and outputs cross phases (agent-coherent accesses); a
 // template parameter so the main loop has one fixed number of loads.
 // ASYM: unsigned codes with a zero point per group (w = q * s + z): each
 // group adds z * (sum of the group's activations) to every output of its row.
 template <int XT, bool GROUPED, int MT, bool COH, bool ASYM = false>
-__device__ __forceinline__ void run_msegment(const StreamPhase& seg, const StreamProblem* probs,
+__device__ __forceinline__ bool run_msegment(const StreamPhase& seg, const StreamProblem* probs,
                                              const StreamProblem& single, int2 wr, int m, uint8_t* smem,
                                              uint32_t* sync, uint32_t wait_target) {
   static_assert(!ASYM || GROUPED, "zero points come per 128-group");
@@ -149,7 +151,7 @@ __device__ __forceinline__ void run_msegment(const StreamPhase& seg, const Strea
   const int32_t GS = (int32_t)(k / 128);
   const int64_t w = blockIdx.x;
   const int32_t r0 = (int32_t)(w * N / G), r1 = (int32_t)((w + 1) * N / G);
-  if (r1 == r0) return;  // uniform
+  if (r1 == r0) return false;  // uniform: no rows here, a pending wait stays pending
   const int nrec = wr.y - wr.x + 1;
 
   ProdRec* rec = reinterpret_cast<ProdRec*>(smem);
@@ -415,6 +417,7 @@ __device__ __forceinline__ void run_msegment(const StreamPhase& seg, const Strea
     pf = next_or_same(pf);
   }
   __syncthreads();  // LDS is reused by the next segment
+  return true;
 }
 
 // variant = (x fp16 ? 0 : 3) + (asymmetric ? 2 : grouped ? 1 : 0); 6 = a mix
@@ -424,29 +427,29 @@ __host__ __device__ inline int mstream_variant(int xt, int group, int asym) {
 constexpr int MVAR_ANY = 6;
 
 template <int MT, int V>
-__device__ __forceinline__ void mrun_variant(const StreamPhase& seg, const StreamProblem* probs,
+__device__ __forceinline__ bool mrun_variant(const StreamPhase& seg, const StreamProblem* probs,
                                              const StreamProblem& single, int2 wr, int m, uint8_t* smem,
                                              uint32_t* sync, uint32_t wt, bool coh) {
   constexpr int XT = V < 3 ? XF16 : XBF16;
   constexpr bool ASYM = V % 3 == 2, GROUPED = V % 3 != 0;
-  if (coh) run_msegment<XT, GROUPED, MT, true, ASYM>(seg, probs, single, wr, m, smem, sync, wt);
-  else run_msegment<XT, GROUPED, MT, false, ASYM>(seg, probs, single, wr, m, smem, sync, wt);
+  if (coh) return run_msegment<XT, GROUPED, MT, true, ASYM>(seg, probs, single, wr, m, smem, sync, wt);
+  return run_msegment<XT, GROUPED, MT, false, ASYM>(seg, probs, single, wr, m, smem, sync, wt);
 }
 
 template <int MT, int VAR>
-__device__ __forceinline__ void mseg_dispatch(const StreamPhase& seg, const StreamProblem* probs,
+__device__ __forceinline__ bool mseg_dispatch(const StreamPhase& seg, const StreamProblem* probs,
                                               const StreamProblem& single, int2 wr, int m, uint8_t* smem,
                                               uint32_t* sync, uint32_t wt, bool coh) {
   if constexpr (VAR != MVAR_ANY) {
-    mrun_variant<MT, VAR>(seg, probs, single, wr, m, smem, sync, wt, coh);
+    return mrun_variant<MT, VAR>(seg, probs, single, wr, m, smem, sync, wt, coh);
   } else {
     switch (mstream_variant(seg.xt, seg.group, seg.asym)) {
-      case 0: mrun_variant<MT, 0>(seg, probs, single, wr, m, smem, sync, wt, coh); break;
-      case 1: mrun_variant<MT, 1>(seg, probs, single, wr, m, smem, sync, wt, coh); break;
-      case 2: mrun_variant<MT, 2>(seg, probs, single, wr, m, smem, sync, wt, coh); break;
-      case 3: mrun_variant<MT, 3>(seg, probs, single, wr, m, smem, sync, wt, coh); break;
-      case 4: mrun_variant<MT, 4>(seg, probs, single, wr, m, smem, sync, wt, coh); break;
-      default: mrun_variant<MT, 5>(seg, probs, single, wr, m, smem, sync, wt, coh); break;
+      case 0: return mrun_variant<MT, 0>(seg, probs, single, wr, m, smem, sync, wt, coh);
+      case 1: return mrun_variant<MT, 1>(seg, probs, single, wr, m, smem, sync, wt, coh);
+      case 2: return mrun_variant<MT, 2>(seg, probs, single, wr, m, smem, sync, wt, coh);
+      case 3: return mrun_variant<MT, 3>(seg, probs, single, wr, m, smem, sync, wt, coh);
+      case 4: return mrun_variant<MT, 4>(seg, probs, single, wr, m, smem, sync, wt, coh);
+      default: return mrun_variant<MT, 5>(seg, probs, single, wr, m, smem, sync, wt, coh);
     }
   }
 }
@@ -467,18 +470,18 @@ __global__ __launch_bounds__(ms_threads<MT>()) void gemm_mstream_kernel(
   bool coh = false;
   for (int s = 0; s < nseg; ++s) coh = coh || segs[s].wait;
   uint32_t waits = 0;
+  uint32_t* pending = nullptr;  // a phase wait not performed yet (see gemv_stream_kernel)
   for (int s = 0; s < nseg; ++s) {
     const StreamPhase seg = segs[s];
-    uint32_t* ws = nullptr;
     if (seg.wait) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
       if (threadIdx.x == 0) __hip_atomic_fetch_add(sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       ++waits;
-      ws = sync;
+      pending = sync;
     }
     const int2 wr = wranges[(int64_t)s * G + blockIdx.x];
-    mseg_dispatch<MT, VAR>(seg, probs, single_prob, wr, m, smem, ws, waits * G, coh);
+    if (mseg_dispatch<MT, VAR>(seg, probs, single_prob, wr, m, smem, pending, waits * G, coh)) pending = nullptr;
   }
   if (waits) {
     __syncthreads();

@@ -182,7 +182,11 @@ __device__ __forceinline__ int rec_of(const ProdRec* rec, int nrec, int32_t row)
 }
 
 // seg: segment description; probs: the problem table (nullptr: `single`);
-// wr: {first, last} problem (within the segment) touched by this workgroup.
+// wr: {first, last} problem (within the segment) touched by this workgroup;
+// sync (non-null): a phase wait this workgroup has not performed yet, done
+// before its first activation load. Returns false when the workgroup has no
+// rows in the segment: it then read nothing, and a pending wait stays pending
+// for its next segment.
 //
 // Work split inside the workgroup: rows [r0, r1) form quads of 4 rows; a
 // quad-step is one 16-chunk column block of a quad (4 x 256 contiguous-row
@@ -190,7 +194,7 @@ __device__ __forceinline__ int rec_of(const ProdRec* rec, int nrec, int32_t row)
 // its 16-lane group q4 handling row 4*quad + q4, so all four groups of a wave
 // cross row ends together: every branch of the main loop is wave-uniform.
 template <int XT, int BITS, bool GROUPED, int MR, bool ASYM = false>
-__device__ __forceinline__ void run_segment(const StreamPhase& seg, const StreamProblem* probs,
+__device__ __forceinline__ bool run_segment(const StreamPhase& seg, const StreamProblem* probs,
                                             const StreamProblem& single, int2 wr, uint8_t* smem,
                                             uint32_t* sync, uint32_t wait_target, bool coherent) {
   using CD = Codes<BITS>;
@@ -223,10 +227,10 @@ __device__ __forceinline__ void run_segment(const StreamPhase& seg, const Stream
   const int64_t rowbytes = (int64_t)C * 16;
   const int32_t GS = (int32_t)(k / 128);
   const int64_t w = blockIdx.x;
-  if (w >= G) return;  // uniform: the segment's rows go to fewer workgroups
+  if (w >= G) return false;  // uniform: the segment's rows go to fewer workgroups
   const int32_t r0 = (int32_t)(w * N / G), r1 = (int32_t)((w + 1) * N / G);
   const int32_t R = r1 - r0;
-  if (R == 0) return;  // uniform: this workgroup has no rows in the segment
+  if (R == 0) return false;  // uniform: this workgroup has no rows in the segment
   const int nrec = wr.y - wr.x + 1;
 
   // ---- LDS layout
@@ -583,6 +587,7 @@ __device__ __forceinline__ void run_segment(const StreamPhase& seg, const Stream
     }
   }
   __syncthreads();  // LDS is reused by the next segment
+  return true;
 }
 
 // variant = (x fp16 ? 0 : 6) + (bits 2/4/8 -> 0/2/4) + (grouped ? 1 : 0);
@@ -594,45 +599,45 @@ __host__ __device__ inline int stream_variant(int xt, int bits, int group, int a
 constexpr int VAR_ANY = 16;
 
 template <int MR, int V>
-__device__ __forceinline__ void run_variant(const StreamPhase& seg, const StreamProblem* probs,
+__device__ __forceinline__ bool run_variant(const StreamPhase& seg, const StreamProblem* probs,
                                             const StreamProblem& single, int2 wr, uint8_t* smem,
                                             uint32_t* sync, uint32_t wt, bool coh) {
   if constexpr (V >= 12) {
     constexpr int XT = V < 14 ? XF16 : XBF16;
     constexpr int BITS = (V & 1) ? 4 : 2;
-    run_segment<XT, BITS, true, MR, true>(seg, probs, single, wr, smem, sync, wt, coh);
+    return run_segment<XT, BITS, true, MR, true>(seg, probs, single, wr, smem, sync, wt, coh);
   } else {
     constexpr int XT = V < 6 ? XF16 : XBF16;
     constexpr int BITS = (V % 6) / 2 == 0 ? 2 : (V % 6) / 2 == 1 ? 4 : 8;
     constexpr bool GROUPED = (V % 2) == 1;
-    run_segment<XT, BITS, GROUPED, MR>(seg, probs, single, wr, smem, sync, wt, coh);
+    return run_segment<XT, BITS, GROUPED, MR>(seg, probs, single, wr, smem, sync, wt, coh);
   }
 }
 
 template <int MR, int VAR>
-__device__ __forceinline__ void seg_dispatch(const StreamPhase& seg, const StreamProblem* probs,
+__device__ __forceinline__ bool seg_dispatch(const StreamPhase& seg, const StreamProblem* probs,
                                              const StreamProblem& single, int2 wr, uint8_t* smem,
                                              uint32_t* sync, uint32_t wt, bool coh) {
   if constexpr (VAR != VAR_ANY) {
-    run_variant<MR, VAR>(seg, probs, single, wr, smem, sync, wt, coh);
+    return run_variant<MR, VAR>(seg, probs, single, wr, smem, sync, wt, coh);
   } else {
     switch (stream_variant(seg.xt, seg.bits, seg.group, seg.asym)) {
-      case 0: run_variant<MR, 0>(seg, probs, single, wr, smem, sync, wt, coh); break;
-      case 1: run_variant<MR, 1>(seg, probs, single, wr, smem, sync, wt, coh); break;
-      case 2: run_variant<MR, 2>(seg, probs, single, wr, smem, sync, wt, coh); break;
-      case 3: run_variant<MR, 3>(seg, probs, single, wr, smem, sync, wt, coh); break;
-      case 4: run_variant<MR, 4>(seg, probs, single, wr, smem, sync, wt, coh); break;
-      case 5: run_variant<MR, 5>(seg, probs, single, wr, smem, sync, wt, coh); break;
-      case 6: run_variant<MR, 6>(seg, probs, single, wr, smem, sync, wt, coh); break;
-      case 7: run_variant<MR, 7>(seg, probs, single, wr, smem, sync, wt, coh); break;
-      case 8: run_variant<MR, 8>(seg, probs, single, wr, smem, sync, wt, coh); break;
-      case 9: run_variant<MR, 9>(seg, probs, single, wr, smem, sync, wt, coh); break;
-      case 10: run_variant<MR, 10>(seg, probs, single, wr, smem, sync, wt, coh); break;
-      case 11: run_variant<MR, 11>(seg, probs, single, wr, smem, sync, wt, coh); break;
-      case 12: run_variant<MR, 12>(seg, probs, single, wr, smem, sync, wt, coh); break;
-      case 13: run_variant<MR, 13>(seg, probs, single, wr, smem, sync, wt, coh); break;
-      case 14: run_variant<MR, 14>(seg, probs, single, wr, smem, sync, wt, coh); break;
-      default: run_variant<MR, 15>(seg, probs, single, wr, smem, sync, wt, coh); break;
+      case 0: return run_variant<MR, 0>(seg, probs, single, wr, smem, sync, wt, coh);
+      case 1: return run_variant<MR, 1>(seg, probs, single, wr, smem, sync, wt, coh);
+      case 2: return run_variant<MR, 2>(seg, probs, single, wr, smem, sync, wt, coh);
+      case 3: return run_variant<MR, 3>(seg, probs, single, wr, smem, sync, wt, coh);
+      case 4: return run_variant<MR, 4>(seg, probs, single, wr, smem, sync, wt, coh);
+      case 5: return run_variant<MR, 5>(seg, probs, single, wr, smem, sync, wt, coh);
+      case 6: return run_variant<MR, 6>(seg, probs, single, wr, smem, sync, wt, coh);
+      case 7: return run_variant<MR, 7>(seg, probs, single, wr, smem, sync, wt, coh);
+      case 8: return run_variant<MR, 8>(seg, probs, single, wr, smem, sync, wt, coh);
+      case 9: return run_variant<MR, 9>(seg, probs, single, wr, smem, sync, wt, coh);
+      case 10: return run_variant<MR, 10>(seg, probs, single, wr, smem, sync, wt, coh);
+      case 11: return run_variant<MR, 11>(seg, probs, single, wr, smem, sync, wt, coh);
+      case 12: return run_variant<MR, 12>(seg, probs, single, wr, smem, sync, wt, coh);
+      case 13: return run_variant<MR, 13>(seg, probs, single, wr, smem, sync, wt, coh);
+      case 14: return run_variant<MR, 14>(seg, probs, single, wr, smem, sync, wt, coh);
+      default: return run_variant<MR, 15>(seg, probs, single, wr, smem, sync, wt, coh);
     }
   }
 }
@@ -657,9 +662,12 @@ __global__ __launch_bounds__(st_threads<MR>()) void gemv_stream_kernel(
   bool coh = false;
   for (int s = 0; s < nseg; ++s) coh = coh || segs[s].wait;
   uint32_t waits = 0;
+  // a phase wait this workgroup has not performed yet: the poll happens in
+  // the first later segment where the workgroup has rows, since segments of
+  // one phase may spread their rows over different numbers of workgroups
+  uint32_t* pending = nullptr;
   for (int s = 0; s < nseg; ++s) {
     const StreamPhase seg = segs[s];
-    uint32_t* ws = nullptr;
     if (seg.wait) {
       // this workgroup's outputs of the previous phase are stored
       // (agent-coherent): wait for them to complete, count the workgroup done
@@ -667,10 +675,10 @@ __global__ __launch_bounds__(st_threads<MR>()) void gemv_stream_kernel(
       __syncthreads();
       if (threadIdx.x == 0) __hip_atomic_fetch_add(sync, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       ++waits;
-      ws = sync;
+      pending = sync;
     }
     const int2 wr = wranges[(int64_t)s * G + blockIdx.x];
-    seg_dispatch<MR, VAR>(seg, probs, single_prob, wr, smem, ws, waits * G, coh);
+    if (seg_dispatch<MR, VAR>(seg, probs, single_prob, wr, smem, pending, waits * G, coh)) pending = nullptr;
   }
   if (waits) {
     // leave the counter at zero for the next run: the last workgroup to get
