@@ -6,8 +6,11 @@ no CPU path: if the library is missing, every call raises.
 """
 from __future__ import annotations
 
+import atexit
 import ctypes
 import os
+import sys
+import weakref
 from dataclasses import dataclass
 
 import torch
@@ -164,8 +167,12 @@ def unpack(W: ZqWeight, dtype: torch.dtype = torch.int8) -> torch.Tensor:
 def gemv(W: ZqWeight, x: torch.Tensor, out: torch.Tensor | None = None,
          out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
     """y[n] = sum_k x[k] * w_deq[n][k] for one activation row x [k]."""
+    if x.numel() < W.k or not x.is_contiguous():
+        raise ValueError(f"x must hold {W.k} contiguous elements")
     if out is None:
         out = torch.empty(W.n, dtype=out_dtype, device=x.device)
+    if out.numel() < W.n or not out.is_contiguous():
+        raise ValueError(f"out must hold {W.n} contiguous elements")
     d = W.desc()
     _check(lib().zq_gemv(ctypes.byref(d), _ptr(x), _DT.get(x.dtype, -1), _ptr(out),
                          _DT.get(out.dtype, -1), _stream(x)), "zq_gemv")
@@ -176,10 +183,12 @@ def gemm(W: ZqWeight, X: torch.Tensor, out: torch.Tensor | None = None,
          out_dtype: torch.dtype = torch.float32) -> torch.Tensor:
     """Y[m][n] = sum_k X[m][k] * w_deq[n][k]; X may have a row stride >= k."""
     m = X.shape[0]
-    assert X.dim() == 2 and X.stride(1) == 1
+    if X.dim() != 2 or X.stride(1) != 1 or X.shape[1] < W.k:
+        raise ValueError(f"X must be [m, >= {W.k}] with contiguous rows")
     if out is None:
         out = torch.empty((m, W.n), dtype=out_dtype, device=X.device)
-    assert out.dim() == 2 and out.stride(1) == 1
+    if out.dim() != 2 or out.stride(1) != 1 or out.shape[0] != m or out.shape[1] < W.n:
+        raise ValueError(f"out must be [{m}, >= {W.n}] with contiguous rows")
     d = W.desc()
     _check(lib().zq_gemm(ctypes.byref(d), _ptr(X), _DT.get(X.dtype, -1), m, X.stride(0), _ptr(out),
                          _DT.get(out.dtype, -1), out.stride(0), _stream(X)), "zq_gemm")
@@ -194,23 +203,47 @@ def gemm_raw(W: ZqWeight, x_ptr: int, x_dtype: int, m: int, ldx: int, y_ptr: int
            "zq_gemm")
 
 
+# Plans still open when the interpreter exits are closed by an atexit hook,
+# which runs before torch's own exit handlers (registered earlier, run later)
+# tear down the device: no HIP call is left for object finalisation.
+_live_plans: "weakref.WeakSet[Plan]" = weakref.WeakSet()
+
+
+def _close_live_plans() -> None:
+    for p in list(_live_plans):
+        try:
+            p.close()
+        except Exception:
+            pass
+
+
+atexit.register(_close_live_plans)
+
+
 class Plan:
     """Many products in one resident launch (zq_plan_*). `problems` is a list of
-    (ZqWeight, X [m, k], Y [m, n], phase); phases must not decrease."""
+    (ZqWeight, X [m, k], Y [m, n], phase); phases must not decrease. Every X
+    and Y has the same m rows (the C-ABI cannot see tensor sizes)."""
 
     def __init__(self, problems):
+        self._h = None
         self._keep = problems  # the plan reads these buffers at every run
         m = problems[0][1].shape[0] if problems[0][1].dim() == 2 else 1
         arr = (_Problem * len(problems))()
         for i, (W, X, Y, phase) in enumerate(problems):
             X2 = X if X.dim() == 2 else X.view(1, -1)
             Y2 = Y if Y.dim() == 2 else Y.view(1, -1)
+            if X2.shape[0] != m or Y2.shape[0] != m:
+                raise ValueError(f"problem {i}: X and Y need {m} rows (got {X2.shape[0]} and {Y2.shape[0]})")
+            if X2.shape[1] < W.k or Y2.shape[1] < W.n or X2.stride(1) != 1 or Y2.stride(1) != 1:
+                raise ValueError(f"problem {i}: X must be [m, >= {W.k}] and Y [m, >= {W.n}], rows contiguous")
             arr[i] = _Problem(W.desc(), _ptr(X2), _DT.get(X2.dtype, -1), X2.stride(0), _ptr(Y2),
                               _DT.get(Y2.dtype, -1), Y2.stride(0), phase)
         h = ctypes.c_void_p()
         _check(lib().zq_plan_create(arr, len(problems), m, ctypes.byref(h)), "zq_plan_create")
         self._h = h
         self.device = problems[0][1].device
+        _live_plans.add(self)
 
     def run(self) -> None:
         _check(lib().zq_plan_run(self._h, torch.cuda.current_stream(self.device).cuda_stream), "zq_plan_run")
@@ -223,7 +256,17 @@ class Plan:
             _check(lib().zq_plan_destroy(self._h), "zq_plan_destroy")
             self._h = None
 
+    def __enter__(self) -> "Plan":
+        return self
+
+    def __exit__(self, *exc) -> None:
+        self.close()
+
     def __del__(self):
+        # no HIP call while the interpreter shuts down: live plans were closed
+        # by the atexit hook, and anything left is freed with the process
+        if sys.is_finalizing():
+            return
         try:
             self.close()
         except Exception:
