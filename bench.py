@@ -10,7 +10,15 @@ starts.
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--config qwen7b-decode]
 
-Prints one JSON line. Other workloads (--config):
+Prints one JSON line. The default run also times, in the same process, the
+other workloads of the pages' benchmark set and adds each as a key of its own
+(each with its roofline fraction; --no-extras skips them):
+  config1_gemv512        the 512 x 512 INT4 GEMV (latency: us per call)
+  config3_batch          the 7B stack's weights at M = 1, 4, 8, 16, 32 bf16 rows
+  config4_qwen32b_decode the Qwen2.5-32B-shaped decode stack, M = 1
+  config5_prefill        the mixed INT2/4/8 prefill stack, M = 2048 (TFLOP/s)
+
+Other workloads (--config) print their own line:
   gemv-512             single 512 x 512 INT4 GEMV, per-tensor scale fp16(0.02)
   qwen7b-batch --m M   the 7B stack at M rows of bf16 activations (M <= 32: one
                        plan launch; M > 32: 32-row chunks of it)
@@ -88,6 +96,8 @@ def parse():
                         "inside the captured graph, so small kernels run side by side (default 4 for "
                         "prefill, 1 otherwise)")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-extras", action="store_true",
+                   help="default workload only: skip the other workloads' keys")
     p.add_argument("--layers", type=int, default=None, help="override the layer count (profiling)")
     return p.parse_args()
 
@@ -143,6 +153,29 @@ class Stack:
         self._args = [(ctypes.byref(d), x.data_ptr(), xt, self.m, x.stride(0), y.data_ptr(), zq.F32,
                        y.stride(0)) for d, (_, x, y) in zip(self._descs, self.launches)]
         self.plan = None
+
+    def with_rows(self, m: int, xdt: str):
+        """the same weights with fresh activations of m rows in xdt (and fp32
+        outputs): a Stack sharing this one's weight tensors"""
+        torch, zq = self.torch, self.zq
+        from weight_quantized_amd import synth
+        other = object.__new__(Stack)
+        other.__dict__.update({k: v for k, v in self.__dict__.items() if k not in ("launches", "plan")})
+        other.m, other.xdt, other.plan = m, xdt, None
+        other.launches, other.flops = [], 0
+        dev = torch.device("cuda:0")
+        for i, (W, _, _) in enumerate(self.launches):
+            x = synth.device_normal((m, W.k), xdt, 5000003 * (i + 1) + m, dev)
+            y = torch.empty((m, W.n), dtype=torch.float32, device=dev)
+            other.launches.append((W, x, y))
+            other.flops += 2 * m * W.n * W.k
+        torch.cuda.synchronize()
+        return other
+
+    def close(self):
+        if self.plan is not None:
+            self.plan.close()
+            self.plan = None
 
     def make_plan(self, order: str):
         """one resident launch per step. chained: the decoder-layer phases
@@ -206,68 +239,101 @@ class Stack:
             yield e0, e1
 
 
-def cpu_baseline(stack: Stack, torch, synth, budget_s: float = 12.0):
-    """The fp64 oracle on the host cores over a bounded sample of the same stack."""
-    from oracle import oracle as O
-    threads = min(len(os.sched_getaffinity(0)), 16)
-    done_bytes = 0
-    cpu_seconds = 0.0
-    wall = 0.0
-    used_layers = 0
+def _host_threads():
+    """(threads to use, nproc): the oracle runs on the CPU share this process
+    is given -- OMP_NUM_THREADS when set (a GPU machine gives each GPU's jobs 16
+    host threads, whatever nproc shows), else every core of its affinity set"""
+    nproc = len(os.sched_getaffinity(0))
+    try:
+        share = int(os.environ.get("OMP_NUM_THREADS", "0"))
+    except ValueError:
+        share = 0
+    return (min(share, nproc) if share > 0 else nproc), nproc
+
+
+def _oracle_jobs(stack: Stack, layer: int, threads: int, xrows: int, torch):
+    """one layer's products split by rows into `threads` lists of oracle calls"""
     per_layer = len(stack.shapes)
-    xdt = stack.xdt
+    jobs = []
+    for W, x, _ in stack.launches[layer * per_layer:(layer + 1) * per_layer]:
+        p = W.packed.cpu().numpy().reshape(W.n, -1)
+        sc = W.scales.view(torch.int16).cpu().numpy().view(np.uint16)
+        zz = None if W.zeros is None else W.zeros.view(torch.int16).cpu().numpy().view(np.uint16).reshape(W.n, -1)
+        xh = x[:xrows].view(torch.int16).cpu().numpy().view(np.uint16)
+        bounds = np.linspace(0, W.n, threads + 1).astype(np.int64)
+        for t in range(threads):
+            r0, r1 = int(bounds[t]), int(bounds[t + 1])
+            if r1 > r0:
+                s_rows = sc if W.group == 0 else sc.reshape(W.n, -1)[r0:r1]
+                z_rows = None if zz is None else zz[r0:r1]
+                jobs.append((p[r0:r1], W.bits, s_rows, z_rows, W.group, r1 - r0, W.k, xh, stack.xdt))
+    return [jobs[i::threads] for i in range(threads)]
+
+
+def _run_oracle(per_thread):
+    from oracle import oracle as O
+
+    def work(js):
+        for (pp, bits, ss, zz, grp, n, k, xh_, xd) in js:
+            if zz is None:
+                O.gemm(pp, bits, ss, grp, n, k, xh_, xd)
+            else:
+                O.gemm_asym(pp, bits, ss, zz, n, k, xh_, xd)
+
+    ths = [threading.Thread(target=work, args=(js,)) for js in per_thread]
+    t0, c0 = time.perf_counter(), time.process_time()
+    for t in ths:
+        t.start()
+    for t in ths:
+        t.join()
+    return time.perf_counter() - t0, time.process_time() - c0
+
+
+def cpu_baseline(stack: Stack, torch, synth, budget_s: float = 12.0):
+    """The fp64 oracle, as it stands, on the host over a bounded sample of the
+    same stack: one thread on the first layer, then the thread share on as
+    many layers as about `budget_s` CPU-seconds take. The oracle releases the
+    GIL (a C library through ctypes), so threads run in parallel."""
+    threads, nproc = _host_threads()
+    per_layer = len(stack.shapes)
     xrows = min(stack.m, 16)  # prefill: 16 token rows (the work is linear in m)
+    layer_bytes = [sum(W.nbytes for W, _, _ in stack.launches[l * per_layer:(l + 1) * per_layer])
+                   for l in range(stack.layers)]
+    layer_flops = [sum(2 * xrows * W.n * W.k for W, _, _ in stack.launches[l * per_layer:(l + 1) * per_layer])
+                   for l in range(stack.layers)]
+    prefill = stack.cfg == "qwen7b-prefill"
+
+    def rate(layers, wall):
+        return (sum(layer_flops[:layers]) / wall / 1e12) if prefill else (sum(layer_bytes[:layers]) / wall / 1e9)
+
+    wall1, cpu1 = _run_oracle(_oracle_jobs(stack, 0, 1, xrows, torch))
+    walls, cpus, used = [], 0.0, 0
     for l in range(stack.layers):
-        jobs = []
-        for W, x, _ in stack.launches[l * per_layer:(l + 1) * per_layer]:
-            p = W.packed.cpu().numpy().reshape(W.n, -1)
-            sc = W.scales.view(torch.int16).cpu().numpy().view(np.uint16)
-            xh = x[:xrows].view(torch.int16).cpu().numpy().view(np.uint16)
-            bounds = np.linspace(0, W.n, threads + 1).astype(np.int64)
-            for t in range(threads):
-                r0, r1 = int(bounds[t]), int(bounds[t + 1])
-                if r1 > r0:
-                    s_rows = sc if W.group == 0 else sc.reshape(W.n, -1)[r0:r1]
-                    z_rows = None if W.zeros is None else \
-                        W.zeros.view(torch.int16).cpu().numpy().view(np.uint16).reshape(W.n, -1)[r0:r1]
-                    jobs.append((p[r0:r1], W.bits, s_rows, z_rows, W.group, r1 - r0, W.k, xh, xdt))
-        # one thread per core; each runs its share of rows of every projection
-        per_thread = [jobs[i::threads] for i in range(threads)]
-
-        def work(js):
-            for (pp, bits, ss, zz, grp, n, k, xh_, xd) in js:
-                if zz is None:
-                    O.gemm(pp, bits, ss, grp, n, k, xh_, xd)
-                else:
-                    O.gemm_asym(pp, bits, ss, zz, n, k, xh_, xd)
-
-        ths = [threading.Thread(target=work, args=(js,)) for js in per_thread]
-        t0 = time.perf_counter()
-        c0 = time.process_time()
-        for t in ths:
-            t.start()
-        for t in ths:
-            t.join()
-        wall += time.perf_counter() - t0
-        cpu_seconds += time.process_time() - c0
-        used_layers += 1
-        done_bytes += sum(W.nbytes for W, _, _ in stack.launches[l * per_layer:(l + 1) * per_layer])
-        if cpu_seconds >= budget_s:
+        w, c = _run_oracle(_oracle_jobs(stack, l, threads, xrows, torch))
+        walls.append(w)
+        cpus += c
+        used += 1
+        if cpus >= budget_s:
             break
-    if stack.cfg == "qwen7b-prefill":
-        flops = sum(2 * xrows * W.n * W.k for W, _, _ in stack.launches[:used_layers * per_layer])
-        value, unit = flops / wall / 1e12, "TFLOP/s"
-    else:
-        value, unit = done_bytes / wall / 1e9, "GB/s"
+    v_all, v_1 = rate(used, sum(walls)), rate(1, wall1)
     cpu_model = ""
     try:
         with open("/proc/cpuinfo") as fh:
             cpu_model = next((ln.split(":", 1)[1].strip() for ln in fh if ln.startswith("model name")), "")
     except OSError:
         pass
-    return {"value": round(value, 4), "unit": unit, "cores": threads, "kind": "oracle", "cpu_model": cpu_model,
-            "sample": f"first {used_layers} of {stack.layers} layers (all {per_layer} projections, "
-                      f"m={xrows} of {stack.m}), {cpu_seconds:.1f} CPU-s over {wall:.2f} s wall"}
+    unit = "TFLOP/s" if prefill else "GB/s"
+    return {"value": round(v_all, 4), "unit": unit, "cores": threads, "kind": "oracle",
+            "nproc": nproc, "os_cpu_count": os.cpu_count(), "cpu_model": cpu_model,
+            "threads_1": {"value": round(v_1, 4), "unit": unit, "threads": 1,
+                          "sample": f"layer 0 (all {per_layer} projections, m={xrows} of {stack.m}), "
+                                    f"{wall1:.2f} s wall"},
+            "threads_all": {"value": round(v_all, 4), "unit": unit, "threads": threads,
+                            "sample": f"first {used} of {stack.layers} layers, {cpus:.1f} CPU-s over "
+                                      f"{sum(walls):.2f} s wall"},
+            "sample": f"first {used} of {stack.layers} layers (all {per_layer} projections, m={xrows} of "
+                      f"{stack.m}) on {threads} threads (the host thread share; nproc {nproc}), "
+                      f"{cpus:.1f} CPU-s over {sum(walls):.2f} s wall"}
 
 
 def copy_bench(a, torch):
@@ -292,6 +358,118 @@ def copy_bench(a, torch):
                       "data": "synthetic", "config": {"workload": "1 GiB device-to-device copy",
                                                       "bytes_read": nbytes, "bytes_written": nbytes}}),
           flush=True)
+
+
+def measure(run, steps: int, warmup: int, torch, settle_s: float = SETTLE_S) -> dict:
+    """untimed settle and warmup, then exactly `steps` runs between two device
+    synchronisations; an event before every run gives per-step times"""
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < settle_s:
+        run()
+        torch.cuda.synchronize()
+    for _ in range(warmup):
+        run()
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    w0 = time.perf_counter()
+    for i in range(steps):
+        ev[i].record()
+        run()
+    ev[steps].record()
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - w0) * 1e3 / steps
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(steps)])
+    # a plan run is one resident launch (decode) or one launch per bit width
+    # (prefill): the per-step intervals of the timed region are its durations
+    return {"ms": ev[0].elapsed_time(ev[steps]) / steps, "ms_median": float(np.median(per)),
+            "ms_mean_of_steps": float(per.mean()), "wall_ms": wall_ms}
+
+
+def decode_figures(stack: Stack, t: dict, kern_ms: float) -> dict:
+    """a decode workload's step time in the four forms (GB/s, us per layer,
+    tok/s equivalent, fraction of the HBM roofline)"""
+    gbs = stack.weight_bytes / (t["ms"] * 1e-3) / 1e9
+    kern_gbs = stack.weight_bytes / (kern_ms * 1e-3) / 1e9
+    return {"value": round(gbs, 1), "unit": "GB/s", "hbm_frac": round(gbs / HBM_PEAK_GBS, 4),
+            "ms_per_step": round(t["ms"], 5), "ms_per_step_median": round(t["ms_median"], 5),
+            "us_per_layer": round(t["ms"] * 1e3 / stack.layers, 3),
+            "tok_s_equiv": round(stack.m / (t["ms"] * 1e-3), 1),
+            "tflop_s": round(stack.flops / (t["ms"] * 1e-3) / 1e12, 2),
+            "roofline": {"bound": "hbm", "achieved": round(kern_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(kern_gbs / HBM_PEAK_GBS, 4)},
+            "weight_bytes_per_step": stack.weight_bytes, "layers": stack.layers, "m": stack.m,
+            "avg_kernel_us": round(kern_ms * 1e3, 3)}
+
+
+def prefill_figures(stack: Stack, t: dict, kern_ms: float) -> dict:
+    tfs = stack.flops / (t["ms"] * 1e-3) / 1e12
+    kern_tfs = stack.flops / (kern_ms * 1e-3) / 1e12
+    return {"value": round(tfs, 2), "unit": "TFLOP/s", "mfma_frac": round(tfs / MFMA_BF16_PEAK_TFS, 4),
+            "ms_per_step": round(t["ms"], 5), "ms_per_step_median": round(t["ms_median"], 5),
+            "us_per_layer": round(t["ms"] * 1e3 / stack.layers, 2),
+            "tok_s_equiv": round(stack.m / (t["ms"] * 1e-3), 1),
+            "roofline": {"bound": "mfma", "achieved": round(kern_tfs, 2), "peak": MFMA_BF16_PEAK_TFS,
+                         "unit": "TFLOP/s", "frac": round(kern_tfs / MFMA_BF16_PEAK_TFS, 4)},
+            "flops_per_step": stack.flops, "layers": stack.layers, "m": stack.m,
+            "bits_per_layer": [stack.launches[l * len(stack.shapes)][0].bits for l in range(stack.layers)],
+            "avg_plan_run_us": round(kern_ms * 1e3, 1)}
+
+
+def extras(a, base: Stack, torch, zq, synth) -> dict:
+    """the other workloads, each timed as a plan (steps scaled to about a
+    second of GPU time each), with their roofline fractions"""
+    out = {}
+    # config 1: the 512 x 512 GEMV, latency-bound (131 KB fit in L2)
+    st = Stack("gemv-512", None, None, torch, zq, synth)
+    st.make_plan("independent")
+    t = measure(st.plan_step, 2000, 50, torch, settle_s=0.05)
+    kern = t["ms_mean_of_steps"]
+    f = decode_figures(st, t, kern)
+    out["config1_gemv512"] = {"us_per_call": round(t["ms"] * 1e3, 3),
+                              "us_per_call_median": round(t["ms_median"] * 1e3, 3),
+                              "kernel_us": round(kern * 1e3, 3), "value": f["value"], "unit": "GB/s",
+                              "roofline": {"bound": "latency", "note": "131,074 weight bytes fit in L2; "
+                                           "µs per call is the figure", "hbm_frac": f["hbm_frac"]},
+                              "workload": "512x512 INT4, per-tensor fp16(0.02), M=1, fp16 x, plan launches "
+                                          "back to back"}
+    st.close()
+    del st
+    # config 3: config 2's weights under continuous batching, bf16 rows
+    batch = {}
+    for m in (1, 4, 8, 16, 32):
+        st = base.with_rows(m, "bf16")
+        st.make_plan("independent")
+        t = measure(st.plan_step, 40, 3, torch, settle_s=0.05)
+        f = decode_figures(st, t, t["ms_mean_of_steps"])
+        batch[f"m{m}"] = {k: f[k] for k in ("value", "unit", "hbm_frac", "us_per_layer", "tok_s_equiv", "tflop_s",
+                                            "ms_per_step", "ms_per_step_median", "roofline")}
+        st.close()
+        del st
+    out["config3_batch"] = {"workload": "Qwen2.5-7B-shaped stack (config 2's weights), INT4 group-128, bf16 x, "
+                                        "one plan per M", "by_m": batch}
+    torch.cuda.empty_cache()
+    # config 4: the 32B stack (16.09 GB of weights)
+    st = Stack("qwen32b-decode", None, None, torch, zq, synth)
+    st.make_plan("independent")
+    t = measure(st.plan_step, 100, 5, torch)
+    f = decode_figures(st, t, t["ms_mean_of_steps"])
+    f["workload"] = "Qwen2.5-32B-shaped decode stack: 64 layers x 7 projections, M=1, INT4 group-128, fp16 x"
+    out["config4_qwen32b_decode"] = f
+    st.close()
+    del st
+    torch.cuda.empty_cache()
+    # config 5: mixed-precision prefill, M = 2048
+    st = Stack("qwen7b-prefill", None, None, torch, zq, synth)
+    st.make_plan("independent")
+    t = measure(st.plan_step, 10, 2, torch)
+    f = prefill_figures(st, t, t["ms_mean_of_steps"])
+    f["workload"] = ("Qwen2.5-7B-shaped prefill stack, per-layer INT2/INT4/INT8 (seeded), per-tensor scale, "
+                     "M=2048, bf16 x, one prefill plan")
+    out["config5_prefill"] = f
+    st.close()
+    del st
+    torch.cuda.empty_cache()
+    return out
 
 
 def main():
@@ -332,48 +510,27 @@ def main():
         run = graph.replay
     else:
         run = stack.step
-    t_settle = time.perf_counter()
-    while time.perf_counter() - t_settle < SETTLE_S:
-        run()
-        torch.cuda.synchronize()
-    for _ in range(a.warmup):
-        run()
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    w0 = time.perf_counter()
-    e0.record()
-    for _ in range(a.steps):
-        run()
-    e1.record()
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - w0) * 1e3 / a.steps
-    ms = e0.elapsed_time(e1) / a.steps
+    t = measure(run, a.steps, a.warmup, torch)
+    ms = t["ms"]
 
-    # ---- per-launch kernel durations (event pairs on the launch stream), same number of steps
-    torch.cuda.synchronize()
-    pairs = []
-    mk = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+    # ---- per-launch kernel durations (event pairs on the launch stream)
     if a.launch == "plan":
-        # the dominant kernel is the plan's single resident launch
-        for _ in range(a.steps):
-            p0, p1 = mk()
-            p0.record()
-            stack.plan_step()
-            p1.record()
-            pairs.append((p0, p1))
+        avg_launch_ms = t["ms_mean_of_steps"]  # the plan's resident launch, one per step
         launches = 1
+        stack.plan.check()
     else:
+        torch.cuda.synchronize()
+        pairs = []
+        mk = lambda: (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
         for _ in range(max(1, min(a.steps, 20))):
             pairs.extend(stack.step_timed_launches(mk))
+        torch.cuda.synchronize()
+        avg_launch_ms = float(np.mean([p0.elapsed_time(p1) for p0, p1 in pairs]))
         launches = len(stack.launches)
-    torch.cuda.synchronize()
-    durs_ms = np.array([p0.elapsed_time(p1) for p0, p1 in pairs])
-    if stack.plan is not None:
-        stack.plan.check()
-    avg_launch_ms = float(durs_ms.mean())
 
     out = {"metric": METRIC, "n_gpus": 1, "steps": a.steps, "warmup": a.warmup,
-           "ms_per_step": round(ms, 5), "higher_is_better": True, "scaling": "weak",
+           "ms_per_step": round(ms, 5), "ms_per_step_median": round(t["ms_median"], 5),
+           "higher_is_better": True, "scaling": "weak",
            "vs_baseline": None, "dtype": "f16" if stack.xdt == "f16" else "bf16", "data": "synthetic"}
     per_layer_us = ms * 1e3 / stack.layers
     if a.config == "qwen7b-prefill":
@@ -416,11 +573,14 @@ def main():
         # queues), one per 32-row chunk (m > 32 on the batched-decode kernel)
         "kernels_per_plan_run": (len({W.bits for W, _, _ in stack.launches}) if stack.m > 64 and stack.group == 0
                                  else -(-stack.m // 32) if stack.m > 32 else 1) if a.launch == "plan" else None,
-        "wall_ms_per_step": round(wall_ms, 5), "avg_kernel_us": round(avg_launch_ms * 1e3, 3),
+        "wall_ms_per_step": round(t["wall_ms"], 5), "avg_kernel_us": round(avg_launch_ms * 1e3, 3),
         "streams": a.streams if a.launch == "graph" else 1,
         "settle_s": SETTLE_S}
     if not a.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(stack, torch, synth)
+    if a.config == "qwen7b-decode" and a.launch == "plan" and a.layers is None and not a.no_extras:
+        out.update(extras(a, stack, torch, zq, synth))
+    stack.close()
     print(json.dumps(out), flush=True)
 
 
