@@ -163,6 +163,25 @@ zq_status zq_pack(const void* w, zq_dtype w_dtype, int64_t n, int64_t k, int bit
                   uint16_t* scales_out, void* stream);
 
 /*
+ * zq_pack_noalloc -- zq_pack for callers that cannot allocate device memory
+ * (code running under stream capture elsewhere in the process, tight serving
+ * loops, harnesses that forbid hipMalloc). Same arguments, results, errors
+ * and synchronous behaviour as zq_pack, bit for bit; it calls no hipMalloc,
+ * hipFree or other allocating routine.
+ *   Scratch: the pack kernels' two flag words (error bits, tensor absmax) live
+ *   in a 256-byte device array inside the library, one copy per GPU, held
+ *   until the process ends; its address is looked up on the first call on
+ *   each device. Every shape that zq_pack accepts fits it (the flags do not
+ *   grow with n or k), so no size is rejected beyond zq_pack's own checks.
+ *   The words are cleared at the start of every call.
+ *   Calls that overlap on one GPU (other host threads or streams) share that
+ *   array and race: serialise them.
+ */
+zq_status zq_pack_noalloc(const void* w, zq_dtype w_dtype, int64_t n, int64_t k, int bits,
+                          int group, const uint16_t* scales_in, void* packed_out,
+                          uint16_t* scales_out, void* stream);
+
+/*
  * zq_unpack -- decode a packed matrix. [wiki, section "Компилятор GPU-ядер":
  * the unpack_int4 intrinsic; this is its signed form for 2, 4 and 8 bits.]
  *   out  device, [n][k] row-major of out_dtype:

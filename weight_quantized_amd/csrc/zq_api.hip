@@ -65,6 +65,96 @@ zq_status check_weight(const zq_weight* W) {
 std::mutex g_dev_mu;
 std::vector<zq::DeviceInfo> g_devs;
 
+// ---- device flag words of the pack kernels: [0] error bits, [1] tensor absmax
+constexpr int PACK_FLAG_WORDS = 2;
+
+// Scratch of zq_pack_noalloc: a file-scope device array, one copy per GPU,
+// holding the pack kernels' flag words (every shape needs the same two).
+// Host code never passes `scratch` itself (in host code the name is only a
+// stand-in); the device address comes from hipGetSymbolAddress, taken once
+// per device with that device current and kept in g_scratch.
+constexpr int NOALLOC_SCRATCH_WORDS = 64;  // 256 bytes per device
+static __device__ __align__(256) uint32_t scratch[NOALLOC_SCRATCH_WORDS];
+std::mutex g_scratch_mu;
+std::vector<uint32_t*> g_scratch;  // per device: address of `scratch`, or null before the first call
+
+hipError_t scratch_address(uint32_t** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if ((int)g_scratch.size() <= dev) g_scratch.resize(dev + 1, nullptr);
+  if (!g_scratch[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch[dev] = static_cast<uint32_t*>(p);
+  }
+  *out = g_scratch[dev];
+  return hipSuccess;
+}
+
+// Argument checks of zq_pack (before any HIP call).
+zq_status check_pack(const void* w, zq_dtype w_dtype, int64_t n, int64_t k, int bits, int group,
+                     const uint16_t* scales_in, void* packed_out, uint16_t* scales_out) {
+  zq_status st = check_format(bits, group, n, k);
+  if (st) return st;
+  if (w_dtype != ZQ_I8 && w_dtype != ZQ_F16 && w_dtype != ZQ_BF16 && w_dtype != ZQ_F32)
+    return fail(ZQ_ERR_INVALID_ARG, "w_dtype=%d not accepted", (int)w_dtype);
+  const bool empty = n == 0 || k == 0;
+  if (!empty && (!w || !packed_out)) return fail(ZQ_ERR_INVALID_ARG, "null w or packed_out");
+  if (w_dtype != ZQ_I8 && !scales_in && !scales_out)
+    return fail(ZQ_ERR_INVALID_ARG, "float weights need scales_in or scales_out");
+  return ZQ_OK;
+}
+
+// The work of zq_pack on checked arguments, with `flags` (PACK_FLAG_WORDS
+// device words, used only for non-empty shapes) as the kernels' flag buffer:
+// cleared by a fill kernel, then read back after the stream is synchronised.
+zq_status pack_body(const void* w, zq_dtype w_dtype, int64_t n, int64_t k, int bits, int group,
+                    const uint16_t* scales_in, void* packed_out, uint16_t* scales_out, void* stream,
+                    uint32_t* flags) {
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t ns = zq_num_scales(group, n, k);
+  hipError_t e;
+  if (scales_in && scales_out && scales_in != scales_out && ns > 0) {
+    e = hipMemcpyAsync(scales_out, scales_in, (size_t)ns * 2, hipMemcpyDeviceToDevice, s);
+    if (e != hipSuccess) return hip_fail(e, "copy scales");
+  }
+  if (n == 0 || k == 0) {
+    if (w_dtype != ZQ_I8 && !scales_in && ns > 0) {
+      // an empty tensor has absmax 0: its scales are +0
+      e = hipMemsetAsync(scales_out, 0, (size_t)ns * 2, s);
+      if (e != hipSuccess) return hip_fail(e, "zero scales");
+    }
+    e = hipStreamSynchronize(s);
+    return e == hipSuccess ? ok() : hip_fail(e, "sync");
+  }
+  zq::PackArgs a;
+  a.w = w;
+  a.wt = (int)w_dtype;
+  a.n = n;
+  a.k = k;
+  a.bits = bits;
+  a.group = group;
+  a.scales = scales_in ? scales_in : scales_out;
+  a.zeros = nullptr;
+  a.packed = (uint8_t*)packed_out;
+  a.flags = flags;
+  a.stream = s;
+  uint32_t host_flags[PACK_FLAG_WORDS] = {0, 0};
+  e = zq::launch_zero_rows(flags, 4, 1, PACK_FLAG_WORDS, PACK_FLAG_WORDS, s);
+  if (e == hipSuccess && w_dtype != ZQ_I8 && !scales_in) e = zq::launch_compute_scales(a, scales_out);
+  if (e == hipSuccess) e = zq::launch_quantize_pack(a);
+  if (e == hipSuccess) e = hipMemcpyAsync(host_flags, flags, sizeof host_flags, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "pack");
+  if (host_flags[0] & zq::FLAG_NONFINITE) return fail(ZQ_ERR_RANGE, "non-finite weight or scale");
+  if (host_flags[0] & zq::FLAG_SCALE_RANGE) return fail(ZQ_ERR_RANGE, "scale beyond the fp16 range");
+  if (host_flags[0] & zq::FLAG_CODE_RANGE) return fail(ZQ_ERR_RANGE, "code outside the %d-bit range", bits);
+  return ok();
+}
+
 }  // namespace
 
 namespace zq {
@@ -113,58 +203,33 @@ const char* zq_last_error(void) { return g_err; }
 
 zq_status zq_pack(const void* w, zq_dtype w_dtype, int64_t n, int64_t k, int bits, int group,
                   const uint16_t* scales_in, void* packed_out, uint16_t* scales_out, void* stream) {
-  zq_status st = check_format(bits, group, n, k);
+  zq_status st = check_pack(w, w_dtype, n, k, bits, group, scales_in, packed_out, scales_out);
   if (st) return st;
-  if (w_dtype != ZQ_I8 && w_dtype != ZQ_F16 && w_dtype != ZQ_BF16 && w_dtype != ZQ_F32)
-    return fail(ZQ_ERR_INVALID_ARG, "w_dtype=%d not accepted", (int)w_dtype);
-  const bool empty = n == 0 || k == 0;
-  if (!empty && (!w || !packed_out)) return fail(ZQ_ERR_INVALID_ARG, "null w or packed_out");
-  if (w_dtype != ZQ_I8 && !scales_in && !scales_out)
-    return fail(ZQ_ERR_INVALID_ARG, "float weights need scales_in or scales_out");
-  hipStream_t s = (hipStream_t)stream;
-  const int64_t ns = zq_num_scales(group, n, k);
-  hipError_t e;
-  if (scales_in && scales_out && scales_in != scales_out && ns > 0) {
-    e = hipMemcpyAsync(scales_out, scales_in, (size_t)ns * 2, hipMemcpyDeviceToDevice, s);
-    if (e != hipSuccess) return hip_fail(e, "copy scales");
-  }
-  if (empty) {
-    if (w_dtype != ZQ_I8 && !scales_in && ns > 0) {
-      // an empty tensor has absmax 0: its scales are +0
-      e = hipMemsetAsync(scales_out, 0, (size_t)ns * 2, s);
-      if (e != hipSuccess) return hip_fail(e, "zero scales");
-    }
-    e = hipStreamSynchronize(s);
-    return e == hipSuccess ? ok() : hip_fail(e, "sync");
-  }
+  if (n == 0 || k == 0) return pack_body(w, w_dtype, n, k, bits, group, scales_in, packed_out, scales_out, stream,
+                                         nullptr);
   uint32_t* flags = nullptr;
-  e = hipMalloc(&flags, 2 * sizeof(uint32_t));
+  hipError_t e = hipMalloc(&flags, PACK_FLAG_WORDS * sizeof(uint32_t));
   if (e != hipSuccess) return hip_fail(e, "hipMalloc flags");
-  zq::PackArgs a;
-  a.w = w;
-  a.wt = (int)w_dtype;
-  a.n = n;
-  a.k = k;
-  a.bits = bits;
-  a.group = group;
-  a.scales = scales_in ? scales_in : scales_out;
-  a.zeros = nullptr;
-  a.packed = (uint8_t*)packed_out;
-  a.flags = flags;
-  a.stream = s;
-  uint32_t host_flags[2] = {0, 0};
-  e = hipMemsetAsync(flags, 0, 2 * sizeof(uint32_t), s);
-  if (e == hipSuccess && w_dtype != ZQ_I8 && !scales_in) e = zq::launch_compute_scales(a, scales_out);
-  if (e == hipSuccess) e = zq::launch_quantize_pack(a);
-  if (e == hipSuccess) e = hipMemcpyAsync(host_flags, flags, sizeof host_flags, hipMemcpyDeviceToHost, s);
-  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  st = pack_body(w, w_dtype, n, k, bits, group, scales_in, packed_out, scales_out, stream, flags);
+  char keep[sizeof g_err];
+  memcpy(keep, g_err, sizeof keep);
   hipError_t ef = hipFree(flags);
-  if (e != hipSuccess) return hip_fail(e, "pack");
+  if (st) return fail(st, "%s", keep);
   if (ef != hipSuccess) return hip_fail(ef, "hipFree flags");
-  if (host_flags[0] & zq::FLAG_NONFINITE) return fail(ZQ_ERR_RANGE, "non-finite weight or scale");
-  if (host_flags[0] & zq::FLAG_SCALE_RANGE) return fail(ZQ_ERR_RANGE, "scale beyond the fp16 range");
-  if (host_flags[0] & zq::FLAG_CODE_RANGE) return fail(ZQ_ERR_RANGE, "code outside the %d-bit range", bits);
   return ok();
+}
+
+zq_status zq_pack_noalloc(const void* w, zq_dtype w_dtype, int64_t n, int64_t k, int bits, int group,
+                          const uint16_t* scales_in, void* packed_out, uint16_t* scales_out, void* stream) {
+  zq_status st = check_pack(w, w_dtype, n, k, bits, group, scales_in, packed_out, scales_out);
+  if (st) return st;
+  static_assert(PACK_FLAG_WORDS <= NOALLOC_SCRATCH_WORDS, "the pack flags fit the static scratch");
+  uint32_t* flags = nullptr;
+  if (n > 0 && k > 0) {
+    hipError_t e = scratch_address(&flags);
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+  }
+  return pack_body(w, w_dtype, n, k, bits, group, scales_in, packed_out, scales_out, stream, flags);
 }
 
 zq_status zq_pack_asym(const void* w, zq_dtype w_dtype, int64_t n, int64_t k, int bits,

@@ -23,7 +23,8 @@ I8, F16, BF16, F32 = 0, 1, 2, 3
 _DT = {torch.int8: I8, torch.float16: F16, torch.bfloat16: BF16, torch.float32: F32}
 
 # every exported symbol of include/zq.h
-SYMBOLS = ("zq_packed_bytes", "zq_num_scales", "zq_pack", "zq_pack_asym", "zq_unpack", "zq_gemv", "zq_gemm",
+SYMBOLS = ("zq_packed_bytes", "zq_num_scales", "zq_pack", "zq_pack_noalloc", "zq_pack_asym", "zq_unpack",
+           "zq_gemv", "zq_gemm",
            "zq_plan_create", "zq_plan_run", "zq_plan_check", "zq_plan_destroy",
            "zq_status_string", "zq_last_error")
 
@@ -63,11 +64,12 @@ def lib() -> ctypes.CDLL:
         L.zq_num_scales.argtypes = [i32, i64, i64]
         L.zq_num_scales.restype = i64
         L.zq_pack.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp, vp, vp]
+        L.zq_pack_noalloc.argtypes = [vp, i32, i64, i64, i32, i32, vp, vp, vp, vp]
         L.zq_pack_asym.argtypes = [vp, i32, i64, i64, i32, vp, vp, vp, vp, vp, vp]
         L.zq_unpack.argtypes = [wp, vp, i32, vp]
         L.zq_gemv.argtypes = [wp, vp, i32, vp, i32, vp]
         L.zq_gemm.argtypes = [wp, vp, i32, i64, i64, vp, i32, i64, vp]
-        for f in ("zq_pack", "zq_pack_asym", "zq_unpack", "zq_gemv", "zq_gemm"):
+        for f in ("zq_pack", "zq_pack_noalloc", "zq_pack_asym", "zq_unpack", "zq_gemv", "zq_gemm"):
             getattr(L, f).restype = i32
         L.zq_plan_create.argtypes = [ctypes.POINTER(_Problem), i32, i64, ctypes.POINTER(vp)]
         L.zq_plan_run.argtypes = [vp, vp]
@@ -138,6 +140,22 @@ def pack(w: torch.Tensor, bits: int, group: int, scales: torch.Tensor | None = N
     _check(lib().zq_pack(_ptr(w), _DT.get(w.dtype, -1), n, k, bits, group, _ptr(sin), _ptr(packed),
                          _ptr(out_scales), _stream(w)), "zq_pack")
     return ZqWeight(bits, group, n, k, packed, out_scales)
+
+
+def pack_into(w: torch.Tensor, bits: int, group: int, packed: torch.Tensor, scales_out: torch.Tensor | None,
+              scales: torch.Tensor | None = None, noalloc: bool = False) -> None:
+    """zq_pack (or, with noalloc, zq_pack_noalloc) into caller-given outputs:
+    packed (uint8, >= packed_bytes) and scales_out (fp16, >= num_scales, or
+    None with int8 codes or given scales). Synchronous."""
+    n, k = w.shape
+    if not w.is_contiguous():
+        raise ValueError("w must be contiguous")
+    if packed.numel() < packed_bytes(bits, n, k) or (scales_out is not None and
+                                                     scales_out.numel() < num_scales(group, n, k)):
+        raise ValueError("output buffers too small")
+    fn = lib().zq_pack_noalloc if noalloc else lib().zq_pack
+    _check(fn(_ptr(w), _DT.get(w.dtype, -1), n, k, bits, group, _ptr(scales), _ptr(packed), _ptr(scales_out),
+              _stream(w)), "zq_pack_noalloc" if noalloc else "zq_pack")
 
 
 def pack_asym(w: torch.Tensor, bits: int, scales: torch.Tensor | None = None,
