@@ -1,4 +1,4 @@
-// zq_prefill.hip -- MFMA kernel for prefill-sized batches (m > 64) with one
+// zq_prefill.hip -- MFMA kernels for prefill-sized batches (m > 64) with one
 // scale per tensor: Y = X * dequant(W)^T, codes of 2, 4 or 8 bits.
 //
 // The ZSE wiki article ("ZSE - open-source движок для запуска LLM локально на
@@ -6,233 +6,300 @@
 // GPU-ядра") lists a dequantizing matmul and a shared-memory tiled matmul, and
 // zQuantize (openclawradar articles, section "Componentes da arquitetura";
 // lavx article, section "Technical Architecture") picks INT2..INT8 per tensor.
-// Prefill is compute-bound (2 * 2048 flop per weight byte at m = 2048), so the
-// design is a bf16/fp16 MFMA GEMM for gfx950 with the dequantization fused
-// into the staging of the weight tile:
-//   * a workgroup (8 waves, 2 x 4) computes a 256 x 256 tile of Y; each wave
-//     128 x 64 as 4 x 2 MFMA 32x32x16 tiles (128 fp32 accumulators per lane,
-//     in the accumulation registers), so two waves share each SIMD and hide
-//     each other's LDS and memory waits;
-//   * K runs in steps of 64. Activations go through LDS: the 256 x 64 tile of
-//     step kt + 2 is loaded into registers while step kt computes, and step
-//     kt + 1 is written to the other of two LDS stages at the end of step kt
-//     (16-byte pieces XOR-swizzled by row: conflict-free writes and MFMA
-//     fragment reads);
-//   * weights bypass LDS (its bandwidth, ~128-155 bytes per clock per CU, is
-//     the other limit of this design): each lane loads the 32 codes of its
-//     own fragment row straight into registers, one step ahead, and decodes
-//     them per MFMA with the magic-number decoder (code + BIAS as an exact
-//     16-bit value, pairs (i, i + E/2) of a packed dword). The activations
-//     are permuted into that same order when staged, so the MFMA sums
-//     x * (q + BIAS) with matching pairs;
-//   * every activation row's sum over K is accumulated while staging; the
-//     epilogue stores s * (acc - BIAS * rowsum).
+// Prefill is compute-bound (2 * 2048 flop per weight byte at m = 2048); the
+// design is a bf16/fp16 MFMA GEMM for gfx950 with the dequantization in the
+// registers that feed the matrix cores:
+//   * a workgroup of 4 waves (one per SIMD) computes a 256 x 256 tile of Y;
+//     wave w owns 64 columns and all 256 rows as 8 x 2 MFMA 32x32x16 tiles
+//     (256 fp32 accumulators per lane, in the accumulation registers), so
+//     each decoded weight fragment feeds 8 MFMAs;
+//   * activations and weight codes move from memory straight into LDS
+//     (buffer loads with the LDS destination, 16 bytes per lane): no
+//     registers, no permutation and no address arithmetic per step;
+//     activations fill a ring of stages shared by the workgroup, each wave's
+//     codes three stages of its own;
+//   * codes are decoded in their natural k order by magic numbers (a code
+//     placed in a binary16 / bfloat16 fraction is an exact value q + bias),
+//     one v_perm_b32 and one v_bitop3 per pair of k; the bias times each
+//     activation row's sum is removed in the epilogue (the row sums come
+//     from one more pass over the staged activations);
+//   * with one wave per SIMD the vector ALU, LDS and load instructions of
+//     each k-step are interleaved between its MFMAs (sched_group_barrier).
 #include <algorithm>
+#include <utility>
 
 #include "zq_device.hpp"
 #include "zq_internal.hpp"
 
 namespace zq {
 
-constexpr int P2_BM = 256, P2_BN = 256, P2_BK = 64;
-constexpr int P2_TILE = 256 * 128;            // bytes of one 256-row x 64-k 16-bit activation tile
-constexpr int P2_LDS = 2 * P2_TILE + 256 * 4;  // two stages + row sums
+constexpr int PF_BM = 256, PF_BN = 256, PF_BK = 64;
+constexpr int PF_STAGE = PF_BM * PF_BK * 2;  // bytes of one activation stage (32 KB)
 
 template <int XT>
-__device__ __forceinline__ f16v p2_mfma(u4 a, u4 b, f16v c) {
+__device__ __forceinline__ f16v pf_mfma(u4 a, u4 b, f16v c) {
   if constexpr (XT == XF16)
     return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(h8, a), __builtin_bit_cast(h8, b), c, 0, 0, 0);
   else
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(b8, a), __builtin_bit_cast(b8, b), c, 0, 0, 0);
 }
 
-// byte offset of 16-byte piece (row r, kc = k/8 within the 64-k step)
-__device__ __forceinline__ int p2_off(int r, int kc) { return r * 128 + ((kc ^ (r & 7)) << 4); }
-
-// Activations of one 16-k span (natural order, p0 = k 0..7, p1 = k 8..15) ->
-// the two 8-element MFMA slots in the decoder's pair order for BITS:
-//   INT4: slot g = k 8g + [0,4,1,5,2,6,3,7]
-//   INT8: slot g = k 8g + [0,2,1,3,4,6,5,7]
-//   INT2: slot g = k 4g + [0,8,1,9,2,10,3,11]
-template <int BITS>
-__device__ __forceinline__ void p2_perm(const u4& p0, const u4& p1, u4& s0, u4& s1) {
-  // INT8: one v_perm_b32 each (byte selectors: 0-3 pick bytes of a, 4-7 of
-  // b). INT2/INT4 keep shift-and-mask forms, which measured faster there.
-  auto lo_lo = [](uint32_t a, uint32_t b) {
-    if constexpr (BITS == 8) return __builtin_amdgcn_perm(b, a, 0x05040100u);
-    else return (a & 0xFFFFu) | (b << 16);
-  };
-  auto hi_hi = [](uint32_t a, uint32_t b) {
-    if constexpr (BITS == 8) return __builtin_amdgcn_perm(b, a, 0x07060302u);
-    else return (a >> 16) | (b & 0xFFFF0000u);
-  };
-  if constexpr (BITS == 4) {
-    s0 = u4{lo_lo(p0[0], p0[2]), hi_hi(p0[0], p0[2]), lo_lo(p0[1], p0[3]), hi_hi(p0[1], p0[3])};
-    s1 = u4{lo_lo(p1[0], p1[2]), hi_hi(p1[0], p1[2]), lo_lo(p1[1], p1[3]), hi_hi(p1[1], p1[3])};
-  } else if constexpr (BITS == 8) {
-    s0 = u4{lo_lo(p0[0], p0[1]), hi_hi(p0[0], p0[1]), lo_lo(p0[2], p0[3]), hi_hi(p0[2], p0[3])};
-    s1 = u4{lo_lo(p1[0], p1[1]), hi_hi(p1[0], p1[1]), lo_lo(p1[2], p1[3]), hi_hi(p1[2], p1[3])};
-  } else {
-    s0 = u4{lo_lo(p0[0], p1[0]), hi_hi(p0[0], p1[0]), lo_lo(p0[1], p1[1]), hi_hi(p0[1], p1[1])};
-    s1 = u4{lo_lo(p0[2], p1[2]), hi_hi(p0[2], p1[2]), lo_lo(p0[3], p1[3]), hi_hi(p0[3], p1[3])};
-  }
-}
-
-// sum of the 8 activations of a piece (v_dot2 against (1, 1))
-template <int XT>
-__device__ __forceinline__ float p2_sum8(const u4& p, float acc) {
-  constexpr uint32_t ONES = XT == XF16 ? 0x3C003C00u : 0x3F803F80u;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) acc = dot2<XT>(p[i], ONES, acc);
-  return acc;
-}
-
-// Codes of one MFMA step kk for a lane's fragment: the lane holds 32 codes of
-// its weight row (k 32g .. 32g+31 of the 64-k step, g = lane / 32) as
-// INT4: one u4, INT8: two u4, INT2: one u2 (in a u4, upper half unused);
-// step kk takes codes 8kk .. 8kk+7 of them, decoded in pair order, which
-// matches activation piece kc = 4g + kk staged by p2_perm.
-//
-// bf16 INT4: a pair (code i, code i + 4) of a dword moves, by one shift (none
-// for i = 0), to bits 3:0 of each 16-bit half; there it is the low fraction
-// bits of the bf16 number 128, whose unit in the last place is 1:
-// (t & M) | 0x4300 is the exact value 128 + u, u = q + 8 the code with its
-// sign bit flipped. The flip folds into the masking, ((t ^ S) & M) | O ==
-// (t & M) ^ ((S & M) ^ O): one v_bitop3 per pair; BIAS = 136.
-// bf16 INT2: a pair (code i, code i + 8) moves to bits 3:2, fraction bits of
-// the bf16 number 32 with unit 1: 32 + u, u = q + 2, BIAS = 34, again one
-// v_bitop3 per pair and a shift for three of the four. (Bits 1:0 under 128
-// cost the same but carry a 4 times larger offset into the fp32 sums, which
-// for INT2's small weights came to a fifth of the tolerance at k = 18944;
-// bits 6:5 under 4 need a fourth shift, 4 % slower.)
-// BIAS is removed in the epilogue. fp16 activations keep the decoder with
-// the offset 16 + u: with 1024 + u the fp32 sums of long rows would carry ten
-// more bits of offset.
-// INT8 (256 code values do not fit a bf16 fraction): byte -> float -> the
-// upper 16 bits, exact; BIAS = 128.
+// Natural-order decode: the 8 codes k0..k7 of one MFMA step become 4 dwords
+// of 16-bit pairs (k 2j, 2j+1) = (q + BE, q + BO), exact. Pairs are built by
+// one v_perm_b32 (the code byte copied to bytes 0 and 2, zeros elsewhere)
+// and one and-xor (v_bitop3): the field mask, the sign flip and the magic
+// exponent. The two halves may use different magic numbers.
 template <int XT, int BITS>
-struct P2Dec {
-  static constexpr bool FAST = XT == XBF16 && BITS <= 4;
-  static constexpr float BIAS = !FAST ? Decoder<XT, BITS>::BIAS : BITS == 4 ? 136.f : 34.f;
-  static constexpr uint32_t M = BITS == 4 ? 0x000F000Fu : 0x000C000Cu;
-  static constexpr uint32_t K = BITS == 4 ? 0x00080008u ^ 0x43004300u : 0x00080008u ^ 0x42004200u;
+struct PfDec;
 
+// INT4. bf16: both nibbles at fraction bits 3:0 under 128 (v >> 4 brings
+// the odd nibble down): 136 + q. fp16: even nibble at bits 3:0 under 1024,
+// odd nibble left at bits 7:4 under 64: 1032 + q, 72 + q; no shift.
+template <int XT>
+struct PfDec<XT, 4> {
+  static constexpr float BE = XT == XBF16 ? 136.f : 1032.f, BO = XT == XBF16 ? 136.f : 72.f;
+  static constexpr uint32_t BW = XT == XBF16 ? 0x43084308u : 0x54806408u;  // (BE, BO) as a 16-bit pair
   static __device__ __forceinline__ u4 frag(const u4 (&c)[2], int kk) {
-    using Dc = Decoder<XT, BITS>;
-    constexpr uint32_t S = Codes<BITS>::SIGNS;
-    if constexpr (FAST && BITS == 4) {
-      const uint32_t v = c[0][kk];
-      return u4{(v & M) ^ K, ((v >> 4) & M) ^ K, ((v >> 8) & M) ^ K, ((v >> 12) & M) ^ K};
-    } else if constexpr (FAST) {
-      const uint32_t v = c[0][kk >> 1] >> ((kk & 1) * 8);  // pairs 0..3 or 4..7
-      return u4{((v << 2) & M) ^ K, (v & M) ^ K, ((v >> 2) & M) ^ K, ((v >> 4) & M) ^ K};
-    } else if constexpr (BITS == 4) {
-      const uint32_t v = c[0][kk] ^ S;
-      return u4{Dc::template pair<0>(v), Dc::template pair<1>(v), Dc::template pair<2>(v), Dc::template pair<3>(v)};
-    } else if constexpr (BITS == 8 && XT == XBF16) {
-      // bytes I and I + 2 of a dword -> exact floats -> their upper halves,
-      // joined by one v_perm_b32
-      const uint32_t v0 = c[kk >> 1][2 * (kk & 1)] ^ S, v1 = c[kk >> 1][2 * (kk & 1) + 1] ^ S;
-      auto pr = [](uint32_t v, int i) __attribute__((always_inline)) {
-        const float lo = (float)((v >> (8 * i)) & 0xFFu), hi = (float)((v >> (8 * (i + 2))) & 0xFFu);
-        return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
-      };
-      return u4{pr(v0, 0), pr(v0, 1), pr(v1, 0), pr(v1, 1)};
-    } else if constexpr (BITS == 8) {
-      const uint32_t v0 = c[kk >> 1][2 * (kk & 1)] ^ S, v1 = c[kk >> 1][2 * (kk & 1) + 1] ^ S;
-      return u4{Dc::template pair<0>(v0), Dc::template pair<1>(v0), Dc::template pair<0>(v1),
-                Dc::template pair<1>(v1)};
+    const uint32_t v = c[0][kk];
+    if constexpr (XT == XBF16) {
+      const uint32_t s = v >> 4;
+      return u4{(__builtin_amdgcn_perm(s, v, 0x0C040C00u) & 0x000F000Fu) ^ 0x43084308u,
+                (__builtin_amdgcn_perm(s, v, 0x0C050C01u) & 0x000F000Fu) ^ 0x43084308u,
+                (__builtin_amdgcn_perm(s, v, 0x0C060C02u) & 0x000F000Fu) ^ 0x43084308u,
+                (__builtin_amdgcn_perm(s, v, 0x0C070C03u) & 0x000F000Fu) ^ 0x43084308u};
     } else {
-      const uint32_t v = c[0][kk >> 1] ^ S;
-      if (kk & 1)
-        return u4{Dc::template pair<4>(v), Dc::template pair<5>(v), Dc::template pair<6>(v), Dc::template pair<7>(v)};
-      return u4{Dc::template pair<0>(v), Dc::template pair<1>(v), Dc::template pair<2>(v), Dc::template pair<3>(v)};
+      return u4{(__builtin_amdgcn_perm(v, v, 0x0C000C00u) & 0x00F0000Fu) ^ 0x54806408u,
+                (__builtin_amdgcn_perm(v, v, 0x0C010C01u) & 0x00F0000Fu) ^ 0x54806408u,
+                (__builtin_amdgcn_perm(v, v, 0x0C020C02u) & 0x00F0000Fu) ^ 0x54806408u,
+                (__builtin_amdgcn_perm(v, v, 0x0C030C03u) & 0x00F0000Fu) ^ 0x54806408u};
     }
   }
 };
 
-// One 256 x 256 tile of Y (rows m0.., columns n0..) by the workgroup's
-// WGM x WGN waves; wave (wm, wn) computes rows 256/WGM * wm.. and columns
-// 256/WGN * wn.. of the tile as FI x FJ MFMA 32x32 tiles. Uses P2_LDS bytes
-// of `smem`; ends with every wave past its last LDS access.
-template <int XT, int BITS, int WGM, int WGN>
-__device__ __forceinline__ void p2_tile(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales,
-                                        int64_t n, int64_t k, const uint16_t* __restrict__ x, int64_t m, int64_t ldx,
+// INT2: a byte holds codes 4j..4j+3 at bits 1:0, 3:2, 5:4, 7:6.
+// bf16: even codes at fraction bits 1:0 under 128, odd codes at bits 3:2 of
+// the upper half under 32 (v >> 4 serves the upper two codes of each byte):
+// 130 + q, 34 + q. fp16: every code at fraction bits 9:8 under 4 (the byte
+// moved to the upper byte of its half, the sources shifted by 0, 2, 4, 6):
+// 6 + q for both halves -- a small offset, so that the fp32 sums of long rows
+// carry little of it.
+template <int XT>
+struct PfDec<XT, 2> {
+  static constexpr float BE = XT == XBF16 ? 130.f : 6.f, BO = XT == XBF16 ? 34.f : 6.f;
+  static constexpr uint32_t BW = XT == XBF16 ? 0x42084302u : 0x46004600u;
+  static __device__ __forceinline__ u4 frag(const u4 (&c)[2], int kk) {
+    const uint32_t v = c[0][kk >> 1];
+    // bytes 2(kk&1) and 2(kk&1)+1 of the dword hold this step's 8 codes
+    const uint32_t j0 = 2 * (kk & 1), j1 = j0 + 1;
+    if constexpr (XT == XBF16) {
+      constexpr uint32_t M = 0x000C0003u, K = 0x42084302u;  // field masks; exponents | sign flips
+      const uint32_t s = v >> 4;
+      auto pr = [&](uint32_t src, uint32_t j) __attribute__((always_inline)) {
+        return (__builtin_amdgcn_perm(src, src, 0x0C000C00u | (j << 16) | j) & M) ^ K;
+      };
+      return u4{pr(v, j0), pr(s, j0), pr(v, j1), pr(s, j1)};
+    } else {
+      constexpr uint32_t M = 0x03000300u, K = 0x46004600u;
+      auto pr = [&](uint32_t lo, uint32_t hi, uint32_t j) __attribute__((always_inline)) {
+        return (__builtin_amdgcn_perm(hi, lo, 0x000C000Cu | ((4 + j) << 24) | (j << 8)) & M) ^ K;
+      };
+      const uint32_t v2 = v >> 2, v4 = v >> 4, v6 = v >> 6;
+      return u4{pr(v, v2, j0), pr(v4, v6, j0), pr(v, v2, j1), pr(v4, v6, j1)};
+    }
+  }
+};
+
+// INT8. bf16: u = q + 128 (sign flip) converted to float exactly, upper
+// halves joined: 128 + q. fp16: the flipped byte in fraction bits 7:0 under
+// 1024: 1152 + q, one v_perm and one xor per pair.
+template <int XT>
+struct PfDec<XT, 8> {
+  static constexpr float BE = XT == XBF16 ? 128.f : 1152.f, BO = BE;
+  static constexpr uint32_t BW = XT == XBF16 ? 0x43004300u : 0x64806480u;
+  static __device__ __forceinline__ u4 frag(const u4 (&c)[2], int kk) {
+    const uint32_t v0 = c[kk >> 1][2 * (kk & 1)], v1 = c[kk >> 1][2 * (kk & 1) + 1];
+    if constexpr (XT == XBF16) {
+      auto pr = [](uint32_t v, int i) __attribute__((always_inline)) {
+        const uint32_t f = v ^ 0x80808080u;
+        const float lo = (float)((f >> (16 * i)) & 0xFFu), hi = (float)((f >> (16 * i + 8)) & 0xFFu);
+        return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+      };
+      return u4{pr(v0, 0), pr(v0, 1), pr(v1, 0), pr(v1, 1)};
+    } else {
+      return u4{__builtin_amdgcn_perm(v0, v0, 0x0C010C00u) ^ 0x64806480u,
+                __builtin_amdgcn_perm(v0, v0, 0x0C030C02u) ^ 0x64806480u,
+                __builtin_amdgcn_perm(v1, v1, 0x0C010C00u) ^ 0x64806480u,
+                __builtin_amdgcn_perm(v1, v1, 0x0C030C02u) ^ 0x64806480u};
+    }
+  }
+};
+
+// byte offset of 16-byte piece kc (k/8 within a 64-k step) of tile row r in
+// a stage: pieces XOR-swizzled by row, so that 8 lanes reading one piece
+// column of 8 consecutive rows hit 8 different bank groups
+// Rows r and r' of one group of 16 (or 8) lanes must land in different
+// 16-byte bank groups: with 64 banks a 128-byte row covers half of them, so
+// even and odd rows of 16 consecutive ones each need 8 distinct positions;
+// with 32 banks, 8 consecutive rows do. sw(r) = (r & 7) ^ ((r >> 3) & 1) does
+// both.
+__device__ __forceinline__ int pf_sw(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+__device__ __forceinline__ int pf_off(int r, int kc) { return r * 128 + ((kc ^ pf_sw(r)) << 4); }
+
+// buffer resource of a raw byte range (gfx9 descriptor: stride 0, data
+// format of a plain 32-bit buffer)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t pf_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+
+// Waits until at most N vector memory instructions of this wave are in
+// flight. The loads here go straight to LDS, which the compiler's own wait
+// counting does not follow: these explicit waits are the only ones that
+// order them, and the memory clobber keeps LDS accesses on their side.
+template <int N>
+__device__ __forceinline__ void pf_wait() {
+  __asm__ volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+// the same, then a workgroup barrier (__syncthreads would wait for all loads)
+template <int N>
+__device__ __forceinline__ void pf_barrier() {
+  __asm__ volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"(N) : "memory");
+}
+
+// One k-step's instructions interleaved: each of its NM MFMAs followed by
+// an even share of the vector ALU (NVALU), LDS read (NDS) and vector memory
+// (NVM) instructions of the same scheduling region, so that they issue while
+// the matrix core is busy (with one wave per SIMD, no other wave fills the
+// gaps). Masks: 0x008 MFMA, 0x002 VALU, 0x100 DS read, 0x020 VMEM read.
+template <int MASK, int N>
+__device__ __forceinline__ void pf_group() {
+  if constexpr (N > 0) __builtin_amdgcn_sched_group_barrier(MASK, N, 0);
+}
+template <int NM, int NVALU, int NDS, int NVM, int... T>
+__device__ __forceinline__ void pf_interleave_seq(std::integer_sequence<int, T...>) {
+  ((pf_group<0x008, 1>(), pf_group<0x100, (T + 1) * NDS / NM - T * NDS / NM>(),
+    pf_group<0x002, (T + 1) * NVALU / NM - T * NVALU / NM>(), pf_group<0x020, (T + 1) * NVM / NM - T * NVM / NM>()),
+   ...);
+}
+template <int NM, int NVALU, int NDS, int NVM>
+__device__ __forceinline__ void pf_interleave() {
+  pf_interleave_seq<NM, NVALU, NDS, NVM>(std::make_integer_sequence<int, NM>{});
+}
+
+// LDS per bit width: activation stages (4, or 3 for INT8) and 3 weight-code
+// stages of 4 waves x (INT2 1 KB, INT4 2 KB, INT8 4 KB)
+__host__ __device__ constexpr int pf_ns(int bits) { return bits == 8 ? 3 : 4; }
+__host__ __device__ constexpr int pf_cstage(int bits) { return bits == 2 ? 4096 : bits == 4 ? 8192 : 16384; }
+__host__ __device__ constexpr int pf_lds(int bits) { return pf_ns(bits) * PF_STAGE + 3 * pf_cstage(bits); }
+
+// One 256 x 256 tile of Y = s * (X * (Q + bias)^T - bias sums), one scale per
+// tensor. Four waves; wave w owns columns 64w..64w+63 of the tile and all 256
+// rows (8 x 2 tiles of MFMA 32x32x16). k a multiple of 64.
+//
+// K runs in steps of 64. Activations and weight codes both move from memory
+// straight into LDS: activations into a ring of 4 stages shared by the
+// workgroup, each wave's codes into two stages of its own. Step kt decodes
+// its weight fragments (from the codes that arrived during step kt - 1),
+// issues the codes of step kt + 1 and the activations of step kt + 2, and
+// computes its 4 MFMA k-steps; in its middle (after k-step 1) it waits until
+// the activations of step kt + 1 are in LDS for every wave, so k-step 3
+// already reads step kt + 1's first fragments. The activation stage written
+// at step kt was last read in step kt - 2, which every wave finished before
+// the middle barrier of step kt - 1.
+template <int XT, int BITS>
+__device__ __forceinline__ void pf_tile(const uint8_t* __restrict__ packed, float scale, int64_t n, int64_t k,
+                                        const uint16_t* __restrict__ x, int64_t m, int64_t ldx,
                                         void* __restrict__ y, int64_t ldy, int yt, int64_t m0, int64_t n0,
                                         uint8_t* smem) {
-  constexpr int NT = 64 * WGM * WGN;
-  constexpr int TM = P2_BM / WGM, TN = P2_BN / WGN, FI = TM / 32, FJ = TN / 32;
-  constexpr int SPT = 1024 / NT;            // 16-k activation spans per thread per step
-  constexpr int CB = 8 * BITS;              // code bytes of one row per 64-k step
-  constexpr int NB = BITS == 8 ? 2 : 1;     // 16-byte code loads per lane per fragment
-  // the thread index goes through an empty asm: in the persistent plan
-  // kernel this keeps lane-dependent offsets from being hoisted out of the
-  // tile loop, where they would hold registers across it (and spill)
+  using D = PfDec<XT, BITS>;
+  constexpr int FI = 8, FJ = 2, NS = pf_ns(BITS), CST = pf_cstage(BITS);
+  constexpr int CB = 8 * BITS;  // code bytes of one row per 64-k step
+  // code loads per fragment: INT2 2 x 4 bytes per lane, INT4 16, INT8 2 x 16
+  constexpr int NCL = BITS == 4 ? 1 : 2;
+  constexpr int CL_BYTES = BITS == 2 ? 4 : 16;
+  // vector memory instructions issued before the middle barrier of a step
+  // (the codes two steps ahead, and with 4 stages the activations too)
+  constexpr int VM_EARLY = FJ * NCL + (pf_ns(BITS) == 4 ? 8 : 0);
   int tid_ = threadIdx.x;
   __asm__ volatile("" : "+v"(tid_));
-  const int tid = tid_, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WGN, wn = wave % WGN;
-  const int g = lane >> 5;
+  const int tid = tid_, lane = tid & 63, l32 = lane & 31, g = lane >> 5;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int KT = (int)(k / PF_BK);
   const int64_t rowbytes = k * BITS / 8;
-  const int64_t KT = k / P2_BK;
-  float* rowsum = reinterpret_cast<float*>(smem + 2 * P2_TILE);
 
-  // activation staging: spans (row = s/4, 16-k span s%4), s = it*NT + tid.
-  // Rows past m re-read row m - 1: they only feed output rows past m, which
-  // are not stored.
-  const uint16_t* xrow[SPT];
+  // ---- activations: wave w moves tile rows 64w..64w+63 of each step into LDS
+  // with 8 direct loads of 8 rows x 128 bytes; lane l of load c lands at
+  // slot l of its 1 KB (row 64w + 8c + l/8, position l%8), so it reads piece
+  // (l%8) ^ (row & 7) of that row. Rows past m re-read row m - 1.
+  const int64_t mrows = m - m0 < PF_BM ? m - m0 : PF_BM;
+  const __amdgpu_buffer_rsrc_t xr = pf_rsrc(x + m0 * ldx, (uint32_t)(mrows * ldx * 2));
+  uint32_t aoff[8];
 #pragma unroll
-  for (int it = 0; it < SPT; ++it) {
-    const int s = it * NT + tid;
-    const int64_t r = m0 + (s >> 2);
-    xrow[it] = x + (r < m ? r : m - 1) * ldx + 16 * (s & 3);
+  for (int c = 0; c < 8; ++c) {
+    const int r = 64 * w + 8 * c + (lane >> 3);
+    aoff[c] = (uint32_t)((r < mrows ? r : mrows - 1) * ldx * 2 + (((lane & 7) ^ pf_sw(r)) << 4));
   }
-  // weight fragments of this wave: rows n0 + TN wn + 32 j + lane % 32, bytes
-  // CB/2 * g of each step
-  const uint8_t* wfr[FJ];
+  // activations of step ks into the stage of step kt
+  auto dma_x = [&](int ks, int kt) __attribute__((always_inline)) {
+    uint8_t* dst = smem + (kt % NS) * PF_STAGE + 64 * w * 128;
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (__attribute__((address_space(3))) void*)(dst + c * 1024), 16,
+                                               aoff[c], ks * (PF_BK * 2), 0, 0);
+  };
+  // ---- weight codes: lane (j, l32, g) takes the CB/2 bytes of row
+  // n0 + 64w + 32j + l32 at byte CB/2 * g of each step (k 32g..32g+31); its
+  // load i of fragment j lands at slot `lane` of 64 * CL_BYTES bytes
+  const int64_t nrows = n - n0 < PF_BN ? n - n0 : PF_BN;
+  const __amdgpu_buffer_rsrc_t wr = pf_rsrc(packed + n0 * rowbytes, (uint32_t)(nrows * rowbytes));
+  uint32_t boff[FJ];
 #pragma unroll
   for (int j = 0; j < FJ; ++j) {
-    const int64_t r = n0 + wn * TN + 32 * j + (lane & 31);
-    wfr[j] = packed + (r < n ? r : n - 1) * rowbytes + (CB / 2) * g;
+    const int r = 64 * w + 32 * j + l32;
+    boff[j] = (uint32_t)((r < nrows ? r : nrows - 1) * rowbytes + (CB / 2) * g);
   }
-
-  // two register sets: tile kt + 2 is loaded while tile kt computes (codes
-  // loaded two steps ahead measured slower: the third set of registers
-  // costs more than the latency it hides)
-  u4 xa0[SPT][2], xa1[SPT][2], wb0[FJ][2], wb1[FJ][2];
-  float rs[SPT];
+  uint8_t* cwave = smem + NS * PF_STAGE + w * (CST / 4);
+  auto dma_codes = [&](int ks, int kt) __attribute__((always_inline)) {
+    uint8_t* dst = cwave + (kt % 3) * CST;
 #pragma unroll
-  for (int it = 0; it < SPT; ++it) rs[it] = 0.f;
-  auto load_x = [&](int64_t kt, u4 (&xa)[SPT][2]) __attribute__((always_inline)) {
+    for (int j = 0; j < FJ; ++j)
 #pragma unroll
-    for (int it = 0; it < SPT; ++it) {
-      const u4* p = reinterpret_cast<const u4*>(xrow[it] + kt * P2_BK);
-      xa[it][0] = *to_global(p);
-      xa[it][1] = *to_global(p + 1);
-    }
+      for (int i = 0; i < NCL; ++i)
+        if constexpr (BITS == 2)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              wr, (__attribute__((address_space(3))) void*)(dst + (j * NCL + i) * 64 * CL_BYTES), 4,
+              boff[j] + i * CL_BYTES, ks * CB, 0, 0);
+        else
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              wr, (__attribute__((address_space(3))) void*)(dst + (j * NCL + i) * 64 * CL_BYTES), 16,
+              boff[j] + i * CL_BYTES, ks * CB, 0, 0);
   };
-  auto load_w = [&](int64_t kt, u4 (&wb)[FJ][2]) __attribute__((always_inline)) {
+  auto read_codes = [&](int kt, u4 (&cb)[FJ][2]) __attribute__((always_inline)) {
+    const uint8_t* src = cwave + (kt % 3) * CST;
 #pragma unroll
     for (int j = 0; j < FJ; ++j) {
-      const uint8_t* q = wfr[j] + kt * CB;
       if constexpr (BITS == 2) {
-        const u2 t = __builtin_nontemporal_load(to_global(reinterpret_cast<const u2*>(q)));
-        wb[j][0] = u4{t[0], t[1], 0u, 0u};
+        const uint32_t d0 = *reinterpret_cast<const uint32_t*>(src + (2 * j) * 256 + lane * 4);
+        const uint32_t d1 = *reinterpret_cast<const uint32_t*>(src + (2 * j + 1) * 256 + lane * 4);
+        cb[j][0] = u4{d0, d1, 0u, 0u};
       } else {
 #pragma unroll
-        for (int i = 0; i < NB; ++i) wb[j][i] = __builtin_nontemporal_load(to_global(reinterpret_cast<const u4*>(q) + i));
+        for (int i = 0; i < NCL; ++i) cb[j][i] = *reinterpret_cast<const u4*>(src + (j * NCL + i) * 1024 + lane * 16);
       }
     }
   };
-  // stage activation span `it` of a tile into LDS stage st
-  auto stage_span = [&](uint8_t* st, const u4 (&xa)[SPT][2], int it) __attribute__((always_inline)) {
-    const int s = it * NT + tid, r = s >> 2, sp = s & 3;
-    const u4 p0 = xa[it][0], p1 = xa[it][1];
-    rs[it] = p2_sum8<XT>(p1, p2_sum8<XT>(p0, rs[it]));
-    u4 s0, s1;
-    p2_perm<BITS>(p0, p1, s0, s1);
-    *reinterpret_cast<u4*>(st + p2_off(r, 2 * sp)) = s0;
-    *reinterpret_cast<u4*>(st + p2_off(r, 2 * sp + 1)) = s1;
+
+  // ---- bias sums: lane l of wave w sums row 64w + l of each stage, two of
+  // its 8 pieces per k-step, positions rotated by lane (conflict-free: even
+  // and odd lanes of 16 read 8 distinct positions each)
+  float bsum = 0.f;
+  const int brow = 64 * w + lane;
+  auto bias_part = [&](const uint8_t* cur, int kk) __attribute__((always_inline)) {
+#pragma unroll
+    for (int p = 2 * kk; p < 2 * kk + 2; ++p) {
+      const u4 pc = *reinterpret_cast<const u4*>(cur + brow * 128 + (((p + (lane >> 1)) & 7) << 4));
+#pragma unroll
+      for (int d = 0; d < 4; ++d) bsum = dot2<XT>(pc[d], D::BW, bsum);
+    }
   };
 
   f16v acc[FI][FJ];
@@ -241,96 +308,143 @@ __device__ __forceinline__ void p2_tile(const uint8_t* __restrict__ packed, cons
 #pragma unroll
     for (int j = 0; j < FJ; ++j) acc[i][j] = f16v{};
 
-  auto read_a = [&](const uint8_t* cur, int kk, u4 (&a)[FI]) __attribute__((always_inline)) {
+  // A fragment of row tile i, k-step kk: row 32i + l32, piece 4g + kk
+  auto read_a = [&](const uint8_t* st, int kk, u4 (&a)[FI]) __attribute__((always_inline)) {
+    const int off = pf_off(l32, 4 * g + kk);
+#pragma unroll
+    for (int i = 0; i < FI; ++i) a[i] = *reinterpret_cast<const u4*>(st + off + i * 32 * 128);
+  };
+  auto mfmas = [&](const u4 (&a)[FI], const u4 (&b)[FJ]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < FI; ++i)
-      a[i] = *reinterpret_cast<const u4*>(cur + p2_off(wm * TM + 32 * i + (lane & 31), 4 * g + kk));
+#pragma unroll
+      for (int j = 0; j < FJ; ++j) acc[i][j] = pf_mfma<XT>(a[i], b[j], acc[i][j]);
   };
-  // one K step: the tile in LDS stage kt & 1 with weight codes `wb`. The
-  // fragments of step kk + 1 are read before the MFMAs of step kk; the
-  // activations of tile kt + 1 (`nxa`) are staged into the other stage
-  // between the MFMA steps.
-  auto kstep = [&](int64_t kt, const u4 (&wb)[FJ][2], const u4 (&nxa)[SPT][2], u4 (&lxa)[SPT][2],
-                   u4 (&lwb)[FJ][2]) __attribute__((always_inline)) {
-    const uint8_t* cur = smem + (kt & 1) * P2_TILE;
-    uint8_t* nxt = smem + ((kt + 1) & 1) * P2_TILE;
-    const bool stage_next = kt + 1 < KT;
-    if (kt + 2 < KT) load_x(kt + 2, lxa);  // tile kt's activations are already staged
-    u4 a0[FI], a1[FI];
-    read_a(cur, 0, a0);
+  auto decode = [&](const u4 (&cb)[FJ][2], int kk, u4 (&b)[FJ]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int kk = 0; kk < 4; ++kk) {
-      u4 (&a)[FI] = (kk & 1) ? a1 : a0;
-      u4 (&an)[FI] = (kk & 1) ? a0 : a1;
-      if (kk < 3) read_a(cur, kk + 1, an);
-      u4 b[FJ];
+    for (int j = 0; j < FJ; ++j) b[j] = D::frag(cb[j], kk);
+  };
+  constexpr int DEC_VALU = BITS == 8 && XT == XBF16 ? 28 : 18;  // decode of one k-step (both fragments)
+
+  u4 a0[FI], a1[FI], b0[FJ], b1[FJ];
+  u4 cb[FJ][2], ncb[FJ][2];
+  // prologue: codes of steps 0 and 1, activations of steps 0 and 1
+  dma_codes(0, 0);
+  dma_codes(KT > 1 ? 1 : 0, 1);
+  dma_x(0, 0);
+  dma_x(KT > 1 ? 1 : 0, 1);
+  pf_barrier<0>();
+  read_codes(0, cb);
+  decode(cb, 0, b0);
+  read_a(smem, 0, a0);
+  // Every step issues the same loads and barriers (past the end they reload
+  // the last step's data into stages nobody reads any more), so the loop
+  // body has no branch and every wait count is exact.
+  for (int kt = 0; kt < KT; ++kt) {
+    const uint8_t* cur = smem + (kt % NS) * PF_STAGE;
+    const uint8_t* nxt = smem + ((kt + 1) % NS) * PF_STAGE;
+    dma_codes(kt + 2 < KT ? kt + 2 : KT - 1, kt + 2);
+    if constexpr (NS == 4) dma_x(kt + 2 < KT ? kt + 2 : KT - 1, kt + 2);
+    // k-step 0: MFMAs on (a0, b0); fetch a1, decode b1, bias, the loads above
+    read_a(cur, 1, a1);
+    decode(cb, 1, b1);
+    bias_part(cur, 0);
+    mfmas(a0, b0);
+    pf_interleave<FI * FJ, DEC_VALU + 8, FI + 2, VM_EARLY>();
+    __builtin_amdgcn_sched_barrier(0);
+    // k-step 1
+    read_a(cur, 2, a0);
+    decode(cb, 2, b0);
+    bias_part(cur, 1);
+    mfmas(a1, b1);
+    pf_interleave<FI * FJ, DEC_VALU + 8, FI + 2, 0>();
+    __builtin_amdgcn_sched_barrier(0);
+    // middle of the step: every load issued before this step is done (the
+    // activations of step kt + 1, the codes of step kt + 1), and every wave
+    // has passed step kt - 1, whose stage this step's loads overwrite
+    pf_barrier<VM_EARLY>();
+    // with 3 stages the activations two steps ahead go out only now: their
+    // stage was read until step kt - 1, which every wave has finished
+    if constexpr (NS == 3) dma_x(kt + 2 < KT ? kt + 2 : KT - 1, kt + 2);
+    // k-step 2: also read the next step's codes
+    read_a(cur, 3, a1);
+    decode(cb, 3, b1);
+    bias_part(cur, 2);
+    read_codes(kt + 1, ncb);
+    mfmas(a0, b0);
+    pf_interleave<FI * FJ, DEC_VALU + 8, FI + 2 + FJ * NCL, NS == 3 ? 8 : 0>();
+    __builtin_amdgcn_sched_barrier(0);
+    // k-step 3: the next step's first fragments
+    read_a(nxt, 0, a0);
+    decode(ncb, 0, b0);
+    bias_part(cur, 3);
+    mfmas(a1, b1);
+    pf_interleave<FI * FJ, DEC_VALU + 8, FI + 2, 0>();
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < FJ; ++j) b[j] = P2Dec<XT, BITS>::frag(wb[j], kk);
-#pragma unroll
-      for (int i = 0; i < FI; ++i)
-#pragma unroll
-        for (int j = 0; j < FJ; ++j) acc[i][j] = p2_mfma<XT>(a[i], b[j], acc[i][j]);
-      // spread this thread's spans over the 4 MFMA steps
-#pragma unroll
-      for (int it = 0; it < SPT; ++it)
-        if (stage_next && (it * 4) / SPT == kk) stage_span(nxt, nxa, it);
-      __builtin_amdgcn_sched_barrier(0);
+    for (int j = 0; j < FJ; ++j) {
+      cb[j][0] = ncb[j][0];
+      cb[j][1] = ncb[j][1];
     }
-    if (kt + 2 < KT) load_w(kt + 2, lwb);  // tile kt's codes are consumed
-    __syncthreads();
-  };
-
-  load_x(0, xa0);
-  load_w(0, wb0);
-  if (KT > 1) {
-    load_x(1, xa1);
-    load_w(1, wb1);
   }
-#pragma unroll
-  for (int it = 0; it < SPT; ++it) stage_span(smem, xa0, it);
+
+  // ---- epilogue: every load done and every wave past the loop; bias sums
+  // to LDS (stage 0), then y = s * acc - s * (bias sum of the row)
+  pf_barrier<0>();
+  float* sb = reinterpret_cast<float*>(smem);
+  sb[brow] = scale * bsum;
   __syncthreads();
-  for (int64_t kt = 0; kt < KT; kt += 2) {
-    kstep(kt, wb0, xa1, xa0, wb0);  // compute tile kt (codes in set 0); stage kt+1 (set 1); load kt+2 into set 0
-    if (kt + 1 < KT) kstep(kt + 1, wb1, xa0, xa1, wb1);
-  }
-
-  // row sums: the 4 spans of a row are 4 consecutive threads
+  // D layout of 32x32: value r of lane l is row 8*(r/4) + 4*(l/32) + r%4,
+  // column l%32. The output type and the edge checks are decided once per
+  // tile, outside the element loops.
+  auto epi = [&]<int YT, bool EDGE>() __attribute__((always_inline)) {
 #pragma unroll
-  for (int it = 0; it < SPT; ++it) {
-    float v = rs[it];
-    v += __shfl_xor(v, 1, 64);
-    v += __shfl_xor(v, 2, 64);
-    if ((tid & 3) == 0) rowsum[it * (NT / 4) + (tid >> 2)] = v;
-  }
-  __syncthreads();
-
-  using Dc = P2Dec<XT, BITS>;
-  const float s = f16_bits_to_float(scales[0]);
-  // D layout of 32x32: value r of lane l is row 8*(r/4) + 4*(l/32) + r%4, column l%32
+    for (int i = 0; i < FI; ++i) {
 #pragma unroll
-  for (int i = 0; i < FI; ++i) {
+      for (int q = 0; q < 4; ++q) {
+        const int rl = 32 * i + 8 * q + 4 * g;
+        const f4 c4 = *reinterpret_cast<const f4*>(sb + rl);
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int rl = wm * TM + 32 * i + 8 * (r / 4) + 4 * (lane >> 5) + (r % 4);
-      const int64_t row = m0 + rl;
-      const float corr = Dc::BIAS * rowsum[rl];
+        for (int rr = 0; rr < 4; ++rr) {
+          const int64_t row = m0 + rl + rr;
 #pragma unroll
-      for (int j = 0; j < FJ; ++j) {
-        const int64_t col = n0 + wn * TN + 32 * j + (lane & 31);
-        if (row < m && col < n) store_y(y, row * ldy + col, s * (acc[i][j][r] - corr), yt);
+          for (int j = 0; j < FJ; ++j) {
+            const int64_t col = n0 + 64 * w + 32 * j + l32;
+            const float v = __builtin_fmaf(scale, acc[i][j][4 * q + rr], -c4[rr]);
+            if (!EDGE || (row < m && col < n)) store_y(y, row * ldy + col, v, YT);
+          }
+        }
       }
     }
+  };
+  const bool edge = m0 + PF_BM > m || n0 + PF_BN > n;
+  if (yt == YF32) {
+    if (edge) epi.template operator()<YF32, true>();
+    else epi.template operator()<YF32, false>();
+  } else if (yt == YF16) {
+    if (edge) epi.template operator()<YF16, true>();
+    else epi.template operator()<YF16, false>();
+  } else {
+    if (edge) epi.template operator()<YBF16, true>();
+    else epi.template operator()<YBF16, false>();
   }
-  __syncthreads();  // the row sums are read: the next tile may reuse the LDS
+  __syncthreads();  // the bias sums are read: the next tile may reuse the LDS
 }
 
-template <int XT, int BITS, int WGM, int WGN>
-__global__ __launch_bounds__(64 * WGM * WGN) void gemm_prefill2_kernel(
-    const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales, int64_t n, int64_t k,
-    const uint16_t* __restrict__ x, int64_t m, int64_t ldx, void* __restrict__ y, int64_t ldy, int yt) {
+
+// Single call: one tile per workgroup. Tile i takes row block i % mtiles and
+// column block i / mtiles, so the row blocks of consecutive workgroups --
+// which the hardware deals out to the 8 XCDs in turn -- keep their
+// activation rows within one XCD's L2 when mtiles is a multiple of 8.
+template <int XT, int BITS>
+__global__ __launch_bounds__(256, 1) void prefill_kernel(const uint8_t* __restrict__ packed,
+                                                         const uint16_t* __restrict__ scales, int64_t n, int64_t k,
+                                                         const uint16_t* __restrict__ x, int64_t m, int64_t ldx,
+                                                         void* __restrict__ y, int64_t ldy, int yt, int mtiles) {
   extern __shared__ __align__(16) uint8_t smem[];
-  p2_tile<XT, BITS, WGM, WGN>(packed, scales, n, k, x, m, ldx, y, ldy, yt, (int64_t)blockIdx.y * P2_BM,
-                              (int64_t)blockIdx.x * P2_BN, smem);
+  const int t = blockIdx.x, mb = t % mtiles, nb = t / mtiles;
+  pf_tile<XT, BITS>(packed, f16_bits_to_float(scales[0]), n, k, x, m, ldx, y, ldy, yt, (int64_t)mb * PF_BM,
+                    (int64_t)nb * PF_BN, smem);
 }
 
 // Prefill plan: the tiles of many products of one bit width in one persistent
@@ -344,10 +458,9 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_prefill2_kernel(
 // workgroup to finish leaves the counters at zero for the next run.
 constexpr int PP_QUEUES = 8;
 
-template <int XT, int BITS, int WGM, int WGN>
-__global__ __launch_bounds__(64 * WGM * WGN) void gemm_prefill_plan_kernel(const PrefillProblem* __restrict__ probs,
-                                                                           int nprob, int64_t total,
-                                                                           uint32_t* __restrict__ sync) {
+template <int XT, int BITS>
+__global__ __launch_bounds__(256, 1) void prefill_plan_kernel(const PrefillProblem* __restrict__ probs, int nprob,
+                                                              int64_t total, uint32_t* __restrict__ sync) {
   extern __shared__ __align__(16) uint8_t smem[];
   __shared__ int s_tile;  // tiles of one plan stay below 2^31
   __shared__ int s_prob;
@@ -378,7 +491,7 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_prefill_plan_kernel(const
     }
     __syncthreads();
     // uniform values: read into scalar registers, so the tile's addressing
-    // stays scalar (LDS reads are taken as per-lane values otherwise)
+    // stays scalar
     const int64_t t = (int64_t)__builtin_amdgcn_readfirstlane(s_tile);
     const int pi = __builtin_amdgcn_readfirstlane(s_prob);
     __syncthreads();  // read before thread 0 takes the next tile
@@ -386,8 +499,8 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_prefill_plan_kernel(const
     const PrefillProblem& pr = probs[pi];
     const int local = (int)(t - pr.tile0), mt = (int)pr.mtiles;
     const int nb = local / mt, mb = local - nb * mt;
-    p2_tile<XT, BITS, WGM, WGN>(pr.packed, pr.scales, pr.n, pr.k, pr.x, pr.m, pr.ldx, pr.y, pr.ldy, pr.yt,
-                                (int64_t)mb * P2_BM, (int64_t)nb * P2_BN, smem);
+    pf_tile<XT, BITS>(pr.packed, f16_bits_to_float(pr.scales[0]), pr.n, pr.k, pr.x, pr.m, pr.ldx, pr.y, pr.ldy,
+                      pr.yt, (int64_t)mb * PF_BM, (int64_t)nb * PF_BN, smem);
   }
   if (threadIdx.x == 0 &&
       __hip_atomic_fetch_add(sync + PP_QUEUES, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1) {
@@ -395,26 +508,25 @@ __global__ __launch_bounds__(64 * WGM * WGN) void gemm_prefill_plan_kernel(const
   }
 }
 
+// The tile addresses its activations and codes through 32-bit buffer
+// offsets from the tile's first row: 256 rows of either must stay below 4 GB.
 bool gemm_prefill2_supported(const GemmArgs& a) {
-  if (a.group != 0 || a.m <= 64 || a.k % P2_BK != 0 || a.k == 0) return false;
+  if (a.group != 0 || a.m <= 64 || a.k % PF_BK != 0 || a.k == 0) return false;
   if (((uintptr_t)a.x & 15) || ((a.ldx * 2) & 15) || ((uintptr_t)a.packed & 15)) return false;
+  if ((int64_t)PF_BM * a.ldx * 2 >= ((int64_t)1 << 32) || (int64_t)PF_BN * a.k * a.bits / 8 >= ((int64_t)1 << 32))
+    return false;
   return true;
 }
 
-#ifndef ZQ_P2_WGM
-#define ZQ_P2_WGM 2
-#define ZQ_P2_WGN 4
-#endif
-
 template <int XT, int BITS>
-static hipError_t p2_launch(const GemmArgs& a) {
-  constexpr int WGM = ZQ_P2_WGM, WGN = ZQ_P2_WGN;
-  const void* fn = reinterpret_cast<const void*>(&gemm_prefill2_kernel<XT, BITS, WGM, WGN>);
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, P2_LDS);
+static hipError_t pf_launch(const GemmArgs& a) {
+  const void* fn = reinterpret_cast<const void*>(&prefill_kernel<XT, BITS>);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, pf_lds(BITS));
   if (e != hipSuccess) return e;
-  const dim3 grid((unsigned)((a.n + P2_BN - 1) / P2_BN), (unsigned)((a.m + P2_BM - 1) / P2_BM));
-  hipLaunchKernelGGL((gemm_prefill2_kernel<XT, BITS, WGM, WGN>), grid, dim3(64 * WGM * WGN), P2_LDS, a.stream,
-                     a.packed, a.scales, a.n, a.k, a.x, a.m, a.ldx, a.y, a.ldy, a.yt);
+  const int mtiles = (int)((a.m + PF_BM - 1) / PF_BM);
+  const int64_t tiles = (int64_t)mtiles * ((a.n + PF_BN - 1) / PF_BN);
+  hipLaunchKernelGGL((prefill_kernel<XT, BITS>), dim3((unsigned)tiles), dim3(256), pf_lds(BITS), a.stream, a.packed,
+                     a.scales, a.n, a.k, a.x, a.m, a.ldx, a.y, a.ldy, a.yt, mtiles);
   return hipGetLastError();
 }
 
@@ -423,13 +535,12 @@ bool prefill_plan_supported(const GemmArgs& a) { return a.zeros == nullptr && ge
 template <int XT, int BITS>
 static hipError_t pp_launch(const PrefillProblem* dev_probs, int nprob, int64_t total, uint32_t* sync,
                             hipStream_t stream) {
-  constexpr int WGM = ZQ_P2_WGM, WGN = ZQ_P2_WGN;
-  const void* fn = reinterpret_cast<const void*>(&gemm_prefill_plan_kernel<XT, BITS, WGM, WGN>);
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, P2_LDS);
+  const void* fn = reinterpret_cast<const void*>(&prefill_plan_kernel<XT, BITS>);
+  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, pf_lds(BITS));
   if (e != hipSuccess) return e;
   const int64_t G = std::min<int64_t>(stream_grid(), total);
-  hipLaunchKernelGGL((gemm_prefill_plan_kernel<XT, BITS, WGM, WGN>), dim3((unsigned)G), dim3(64 * WGM * WGN),
-                     P2_LDS, stream, dev_probs, nprob, total, sync);
+  hipLaunchKernelGGL((prefill_plan_kernel<XT, BITS>), dim3((unsigned)G), dim3(256), pf_lds(BITS), stream, dev_probs,
+                     nprob, total, sync);
   return hipGetLastError();
 }
 
@@ -447,13 +558,13 @@ hipError_t launch_prefill_plan(const PrefillProblem* dev_probs, int nprob, int64
 
 hipError_t launch_gemm_prefill2(const GemmArgs& a) {
   if (a.xt == XF16) {
-    if (a.bits == 2) return p2_launch<XF16, 2>(a);
-    if (a.bits == 4) return p2_launch<XF16, 4>(a);
-    return p2_launch<XF16, 8>(a);
+    if (a.bits == 2) return pf_launch<XF16, 2>(a);
+    if (a.bits == 4) return pf_launch<XF16, 4>(a);
+    return pf_launch<XF16, 8>(a);
   }
-  if (a.bits == 2) return p2_launch<XBF16, 2>(a);
-  if (a.bits == 4) return p2_launch<XBF16, 4>(a);
-  return p2_launch<XBF16, 8>(a);
+  if (a.bits == 2) return pf_launch<XBF16, 2>(a);
+  if (a.bits == 4) return pf_launch<XBF16, 4>(a);
+  return pf_launch<XBF16, 8>(a);
 }
 
 }  // namespace zq
