@@ -157,13 +157,13 @@ def problems(entries):
 PLAN_CASES = [
     # m, entries, status, detail
     (0, [(dict(), zq.F16, 0)], zq.ERR_UNSUPPORTED, "m >= 1"),
-    # prefill plans (m > 64, one scale per tensor): one phase, one x dtype
+    # prefill plans (m > 64, symmetric codes): one phase, one x dtype
     (128, [(dict(group=0), zq.BF16, 0), (dict(group=0), zq.BF16, 1)], zq.ERR_UNSUPPORTED, "one phase"),
     (128, [(dict(group=0), zq.BF16, 0), (dict(group=0), zq.F16, 0)], zq.ERR_UNSUPPORTED, "one activation type"),
     (128, [(dict(group=0, k=200), zq.BF16, 0)], zq.ERR_UNSUPPORTED, "multiple of 64"),
-    # mid-batch plans (m > 32 otherwise): INT4 with k a multiple of 512 only
+    # mid-batch plans (32 < m <= 64): INT4 with k a multiple of 512 only
     (48, [(dict(bits=8), zq.F16, 0)], zq.ERR_UNSUPPORTED, "INT4"),
-    (100, [(dict(bits=4, k=384), zq.BF16, 0)], zq.ERR_UNSUPPORTED, "multiple of 512"),
+    (60, [(dict(bits=4, k=384), zq.BF16, 0)], zq.ERR_UNSUPPORTED, "multiple of 512"),
     (40, [(dict(bits=2), zq.BF16, 0)], zq.ERR_UNSUPPORTED, "INT4"),
 ]
 

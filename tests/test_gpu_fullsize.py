@@ -6,8 +6,8 @@ and activation rows are copied back and recomputed by the fp64 oracle.
     Qwen2.5-7B decode stack with asymmetric INT4 weights, plan
     one rank's share of the 7B decode stack under 4-way tensor parallelism, plan
     Qwen2.5-32B decode stack  (64 layers x 7, M = 1), plan
-    7B stack, M = 4, 8, 32 and 128 (bf16 x), plan (MFMA batched-decode kernel,
-    in 32-row chunks past 32)
+    7B stack, M = 4, 8, 32 (bf16 x), plan (MFMA batched-decode kernel), and
+    M = 128, 512, plan (group-scaled prefill tiles)
     7B prefill stack (per-layer INT2/4/8, per-tensor scale, M = 2048, bf16 x),
     plan (tile queues) and graph over 4 streams
 """
@@ -71,14 +71,14 @@ def split_rows(stack, order="independent"):
     """Rows where the work of the plan that bench.py times is split, per
     product index: the first and last row of every workgroup's range and of
     every 256-row block, the rows of quads whose steps are split between two
-    waves (vector-ALU decode kernel), and 256-row tile edges (prefill). This
+    waves (vector-ALU decode kernel), and 256-column tile edges (prefill). This
     mirrors the kernels' documented split (segments of one format, rows
     [w*N/G, (w+1)*N/G) of a segment for workgroup w, equal runs of quad-steps
     per wave) so that the sampled check always covers the seams."""
     ncu = torch.cuda.get_device_properties(0).multi_processor_count
     L = stack.launches
     out = {i: set() for i in range(len(L))}
-    if stack.m > 64 and stack.group == 0:  # prefill tiles
+    if stack.m > 64 and all(W.zeros is None for W, _, _ in L):  # prefill tiles
         for i, (W, _, _) in enumerate(L):
             for t in range(0, W.n, 256):
                 out[i].update({t, min(t + 255, W.n - 1)})
@@ -149,8 +149,8 @@ def check_sampled(stack, n_rows=6, m_rows=None, seed=0, seams=None):
     for idx, (W, x, y) in enumerate(stack.launches):
         extra = sorted(seams[idx]) if seams else []
         rows = np.unique(np.concatenate([[0, W.n - 1], g.integers(0, W.n, n_rows), extra]).astype(np.int64))
-        # prefill: activation rows at every 256-row tile edge besides the random ones
-        edges = [r for t in range(0, stack.m, 256) for r in (t, min(t + 255, stack.m - 1))]
+        # prefill: activation rows at every 128-row tile edge besides the random ones
+        edges = [r for t in range(0, stack.m, 128) for r in (t, min(t + 127, stack.m - 1))]
         ms = np.arange(stack.m) if m_rows is None else np.unique(
             np.concatenate([[0, stack.m - 1], g.integers(0, stack.m, m_rows), edges]).astype(np.int64))
         rowbytes = W.k * W.bits // 8
@@ -215,13 +215,14 @@ def test_qwen32b_decode_plan(mods):
     torch.cuda.empty_cache()
 
 
-@pytest.mark.parametrize("m", [4, 8, 32, 128])
+@pytest.mark.parametrize("m", [4, 8, 32, 128, 512])
 def test_qwen7b_batch_plan(mods, m):
-    # m = 128: four 32-row chunks, each a plan launch over all 196 products
+    # m = 128, 512: group-scaled prefill tiles, one persistent launch
     bench, zq = mods
     stack = bench.Stack("qwen7b-batch", m, None, torch, zq, synth)
     run_step(bench, stack, "plan")
-    check_sampled(stack, n_rows=4, seams=split_rows(stack))
+    # past 64 rows: sampled activation rows too (with every 128-row tile edge)
+    check_sampled(stack, n_rows=4, m_rows=6 if m > 64 else None, seams=split_rows(stack))
 
 
 def test_qwen7b_prefill_plan(mods):

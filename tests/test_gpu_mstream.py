@@ -158,8 +158,8 @@ def test_mstream_plan_rejects_other_formats():
 
 
 # ---------------------------------------------------------------------------
-# mid-batch m (32 < m): 32-row chunks on the batched-decode kernel (group
-# scales at any m, per-tensor scales up to 64), single calls and plans
+# mid-batch m (32 < m <= 64): 32-row chunks on the batched-decode kernel,
+# single calls and plans; past 64 rows the prefill tile takes symmetric codes
 
 
 def chunks(m):
@@ -183,7 +183,7 @@ def test_midbatch_matches_oracle_and_row_chunks(xdt, group, m):
     Y = zq.gemm(W, X)
     torch.cuda.synchronize()
     check(Y.double().cpu().numpy(), O.gemm(p, 4, s, group, n, k, x, xdt), x, xdt, q, group, s, what=f"m={m}")
-    if group or m <= 64:
+    if m <= 64:
         for r0, mc in chunks(m):  # each chunk is a batched-decode call on those rows
             assert torch.equal(Y[r0:r0 + mc], zq.gemm(W, X[r0:r0 + mc])), f"rows {r0}..{r0 + mc}"
 
@@ -205,6 +205,9 @@ def test_midbatch_plan_matches_oracle_and_single_calls(m):
     for (W, X, Y, _), (q, s, p, x, group, n, k) in zip(probs, refs):
         check(Y.double().cpu().numpy(), O.gemm(p, 4, s, group, n, k, x, "bf16"), x, "bf16", q, group, s,
               what=f"n={n}")
+        if m > 64:  # a prefill plan: the single calls' tiles
+            assert torch.equal(Y, zq.gemm(W, X))
+            continue
         for r0, mc in chunks(m):
             assert torch.equal(Y[r0:r0 + mc], zq.gemm(W, X[r0:r0 + mc]))
 

@@ -1,6 +1,7 @@
-"""The prefill MFMA kernel (m > 64, one scale per tensor, k a multiple of 64)
-against the fp64 oracle: ragged tiles, every code width, both activation
-types, and bit-exact integer cases."""
+"""The prefill MFMA kernel (m > 64, symmetric codes; one scale per tensor with
+k a multiple of 64, or one per row and 128 k) against the fp64 oracle:
+ragged tiles, every code width, both activation types, zero and negative
+group scales, and bit-exact integer cases."""
 import numpy as np
 import pytest
 import torch
@@ -23,14 +24,27 @@ def _lib():
     zq = _zq
 
 
-def weight(bits, n, k, seed, codes=None, scale=None):
+def weight(bits, n, k, seed, codes=None, scale=None, group=0):
+    """codes (uniform unless given) and fp16 scale patterns: |N(0,1)| * 0.01 +
+    1e-3, or the given pattern(s)"""
     g = synth.rng(seed)
     q = synth.codes_uniform(g, n, k, bits) if codes is None else codes
-    s = synth.scales_abs_normal(g, 1) if scale is None else np.array([scale], dtype=np.uint16)
+    ns = 1 if group == 0 else n * (k // group)
+    if scale is None:
+        s = synth.scales_abs_normal(g, ns)
+    else:
+        s = np.broadcast_to(np.asarray(scale, dtype=np.uint16), (ns,)).copy()
     p = O.pack(q, bits)
-    W = zq.ZqWeight(bits, 0, n, k, torch.from_numpy(p.reshape(-1)).to(DEV),
+    W = zq.ZqWeight(bits, group, n, k, torch.from_numpy(p.reshape(-1)).to(DEV),
                     torch.from_numpy(s.view(np.float16)).to(DEV))
     return q, s, p, W
+
+
+def check(Y, yref, x, xdt, q, group, s, what=""):
+    xn = np.sqrt((x64(x, xdt) ** 2).sum(1))[:, None]
+    tol = 2e-3 * xn * np.abs(O.dequant(q, group, s)).max(1)[None, :] + 1e-3 * np.abs(yref)
+    err = np.abs(Y - yref)
+    assert np.all(err <= tol), f"{what}: {int((err > tol).sum())} out of tolerance, first {np.argwhere(err > tol)[:3]}"
 
 
 def x_dev(x, xdt):
@@ -54,24 +68,63 @@ def test_prefill_matches_oracle(xdt, bits, m, n, k):
     x = synth.normal(synth.rng(seed + 1), (m, k), xdt)
     Y = zq.gemm(W, x_dev(x, xdt))
     torch.cuda.synchronize()
-    yref = O.gemm(p, bits, s, 0, n, k, x, xdt)
-    xn = np.sqrt((x64(x, xdt) ** 2).sum(1))[:, None]
-    tol = 2e-3 * xn * np.abs(O.dequant(q, 0, s)).max(1)[None, :] + 1e-3 * np.abs(yref)
-    err = np.abs(Y.double().cpu().numpy() - yref)
-    assert np.all(err <= tol), f"{np.argwhere(err > tol)[:3]}"
+    check(Y.double().cpu().numpy(), O.gemm(p, bits, s, 0, n, k, x, xdt), x, xdt, q, 0, s)
+
+
+# group scales: m = 65..520 with ragged row and column tiles (128 x 256)
+@pytest.mark.parametrize("xdt", ["f16", "bf16"])
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("m,n,k", [(65, 100, 128), (128, 256, 256), (200, 600, 1024), (257, 300, 3584),
+                                   (520, 260, 512)])
+def test_prefill_group_matches_oracle(xdt, bits, m, n, k):
+    seed = 17 * m + 5 * n + k + bits + (xdt == "bf16")
+    q, s, p, W = weight(bits, n, k, seed, group=128)
+    x = synth.normal(synth.rng(seed + 1), (m, k), xdt)
+    Y = zq.gemm(W, x_dev(x, xdt))
+    torch.cuda.synchronize()
+    check(Y.double().cpu().numpy(), O.gemm(p, bits, s, 128, n, k, x, xdt), x, xdt, q, 128, s)
 
 
 @pytest.mark.parametrize("xdt", ["f16", "bf16"])
 @pytest.mark.parametrize("bits", [2, 4, 8])
-def test_prefill_integer_inputs_bit_exact(xdt, bits):
+def test_prefill_group_zero_and_negative_scales(xdt, bits):
+    # whole groups with scale 0 (they add nothing; the accumulators keep the
+    # previous group's units) and negative scales, also at a row's first and
+    # last group
+    m, n, k = 150, 300, 1280
+    g = synth.rng(60 + bits)
+    s = synth.scales_abs_normal(g, n * k // 128).reshape(n, k // 128)
+    s[g.random(s.shape) < 0.15] = 0
+    s[:, 0][g.random(n) < 0.3] = 0
+    s[:, -1][g.random(n) < 0.3] = 0
+    s[:7] = 0  # rows with no nonzero scale
+    neg = g.random(s.shape) < 0.2
+    s[neg] |= 0x8000
+    q, s, p, W = weight(bits, n, k, 61 + bits, scale=s.reshape(-1), group=128)
+    x = synth.normal(synth.rng(62 + bits), (m, k), xdt)
+    Y = zq.gemm(W, x_dev(x, xdt))
+    torch.cuda.synchronize()
+    Yn = Y.double().cpu().numpy()
+    check(Yn, O.gemm(p, bits, s, 128, n, k, x, xdt), x, xdt, q, 128, s)
+    assert np.all(Yn[:, :7] == 0)
+
+
+@pytest.mark.parametrize("xdt", ["f16", "bf16"])
+@pytest.mark.parametrize("bits", [2, 4, 8])
+@pytest.mark.parametrize("group", [0, 128])
+def test_prefill_integer_inputs_bit_exact(xdt, bits, group):
+    # integer activations; scale 0.5 per tensor, or 0.5 / 1 / 0 per group:
+    # every partial sum is exact in fp32, and so is every change of units
     m, n, k = 300, 270, 1024
-    g = synth.rng(40 + bits)
-    q, s, p, W = weight(bits, n, k, 0, codes=synth.codes_uniform(g, n, k, bits), scale=0x3800)
+    g = synth.rng(40 + bits + group)
+    scale = 0x3800 if group == 0 else g.choice(np.array([0x3800, 0x3C00, 0x0000], dtype=np.uint16),
+                                                size=n * k // 128, p=[0.45, 0.45, 0.1])
+    q, s, p, W = weight(bits, n, k, 0, codes=synth.codes_uniform(g, n, k, bits), scale=scale, group=group)
     v = g.integers(-4, 5, size=(m, k)).astype(np.float32)
     x = v.astype(np.float16) if xdt == "f16" else synth.f32_to_bf16_bits(v)
     Y = zq.gemm(W, x_dev(x, xdt))
     torch.cuda.synchronize()
-    assert np.array_equal(Y.double().cpu().numpy(), O.gemm(p, bits, s, 0, n, k, x, xdt))
+    assert np.array_equal(Y.double().cpu().numpy(), O.gemm(p, bits, s, group, n, k, x, xdt))
 
 
 def test_prefill_strided_rows_and_low_precision_out():
@@ -83,10 +136,7 @@ def test_prefill_strided_rows_and_low_precision_out():
     Yb = zq.gemm(W, X, out_dtype=torch.bfloat16)
     torch.cuda.synchronize()
     x = np.ascontiguousarray(xf[:, :k])
-    yref = O.gemm(p, 4, s, 0, n, k, x, "bf16")
-    xn = np.sqrt((x64(x, "bf16") ** 2).sum(1))[:, None]
-    tol = 2e-3 * xn * np.abs(O.dequant(q, 0, s)).max(1)[None, :] + 1e-3 * np.abs(yref)
-    assert np.all(np.abs(Y32.double().cpu().numpy() - yref) <= tol)
+    check(Y32.double().cpu().numpy(), O.gemm(p, 4, s, 0, n, k, x, "bf16"), x, "bf16", q, 0, s)
     assert torch.equal(Yb, Y32.to(torch.bfloat16))
 
 
@@ -97,21 +147,22 @@ def test_prefill_strided_rows_and_low_precision_out():
 
 def plan_problems(m, shapes, xdt, seed):
     probs, refs = [], []
-    for i, (bits, n, k) in enumerate(shapes):
-        q, s, p, W = weight(bits, n, k, seed + 10 * i)
+    for i, (bits, n, k, group) in enumerate(shapes):
+        q, s, p, W = weight(bits, n, k, seed + 10 * i, group=group)
         x = synth.normal(synth.rng(seed + 10 * i + 1), (m, k), xdt)
         Y = torch.full((m, n), float("nan"), device=DEV)
         probs.append((W, x_dev(x, xdt), Y, 0))
-        refs.append((q, s, p, x, bits, n, k))
+        refs.append((q, s, p, x, bits, n, k, group))
     return probs, refs
 
 
 @pytest.mark.parametrize("xdt", ["f16", "bf16"])
 def test_prefill_plan_matches_single_calls_and_oracle(xdt):
-    # mixed bit widths and k, ragged m and n tiles; three runs (the counters
-    # must come back to zero after each)
+    # mixed bit widths, k and scale kinds (a queue each), ragged m and n
+    # tiles; three runs (the counters must come back to zero after each)
     m = 300
-    shapes = [(4, 600, 1024), (2, 256, 192), (8, 100, 512), (4, 513, 64), (2, 70, 1024), (8, 260, 256)]
+    shapes = [(4, 600, 1024, 0), (2, 256, 192, 0), (8, 100, 512, 0), (4, 513, 64, 0), (2, 70, 1024, 0),
+              (8, 260, 256, 0), (4, 700, 1024, 128), (2, 300, 256, 128), (8, 130, 384, 128), (4, 60, 128, 128)]
     probs, refs = plan_problems(m, shapes, xdt, seed=700 + (xdt == "bf16"))
     plan = zq.Plan(probs)
     for _ in range(3):
@@ -120,18 +171,16 @@ def test_prefill_plan_matches_single_calls_and_oracle(xdt):
         plan.run()
         torch.cuda.synchronize()
         plan.check()
-        for (W, X, Y, _), (q, s, p, x, bits, n, k) in zip(probs, refs):
+        for (W, X, Y, _), _r in zip(probs, refs):
             # the same tile code as the single-launch kernel: identical outputs
             assert torch.equal(zq.gemm(W, X), Y)
-    for (W, X, Y, _), (q, s, p, x, bits, n, k) in zip(probs, refs):
-        yref = O.gemm(p, bits, s, 0, n, k, x, xdt)
-        xn = np.sqrt((x64(x, xdt) ** 2).sum(1))[:, None]
-        tol = 2e-3 * xn * np.abs(O.dequant(q, 0, s)).max(1)[None, :] + 1e-3 * np.abs(yref)
-        assert np.all(np.abs(Y.double().cpu().numpy() - yref) <= tol), f"bits={bits} n={n} k={k}"
+    for (W, X, Y, _), (q, s, p, x, bits, n, k, group) in zip(probs, refs):
+        check(Y.double().cpu().numpy(), O.gemm(p, bits, s, group, n, k, x, xdt), x, xdt, q, group, s,
+              what=f"bits={bits} n={n} k={k} group={group}")
 
 
 def test_prefill_plan_more_tiles_than_workgroups_integer_exact():
-    # INT4: 128 + 160 tiles, more than the 256 workgroups, so some take two;
+    # INT4: 256 + 320 tiles, more than the 512 workgroups, so some take two;
     # integer activations and scale 1.0 make every output exact
     m = 512
     probs, refs = [], []
@@ -164,9 +213,10 @@ def test_prefill_plan_validation():
     with pytest.raises(zq.ZqError) as e:  # two activation types
         zq.Plan([(W, X, Y, 0), (W, Xh, torch.empty((128, 64), device=DEV), 0)])
     assert e.value.status == zq.ERR_UNSUPPORTED
-    Wg = zq.ZqWeight(4, 128, 64, 256, W.packed, torch.ones(64 * 2, dtype=torch.float16, device=DEV))
-    with pytest.raises(zq.ZqError) as e:  # group scales
-        zq.Plan([(Wg, X, Y, 0)])
+    _, _, _, W8 = weight(8, 64, 192, seed=4)
+    X192 = torch.zeros((128, 200), dtype=torch.bfloat16, device=DEV)[:, 3:195]
+    with pytest.raises(zq.ZqError) as e:  # activations not 16-byte aligned
+        zq.Plan([(W8, X192, Y, 0)])
     assert e.value.status == zq.ERR_UNSUPPORTED
     X48 = torch.zeros((48, 256), dtype=torch.bfloat16, device=DEV)
     with pytest.raises(zq.ZqError) as e:  # 32 < m <= 64

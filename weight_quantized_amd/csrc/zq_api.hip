@@ -349,9 +349,10 @@ zq_status zq_gemm(const zq_weight* W, const void* X, zq_dtype x_dtype, int64_t m
   const bool asym = W->zeros != nullptr;
   const bool use_mstream = m >= zq::MSTREAM_MIN_M &&
                            zq::mstream_supported(W->packed, W->scales, W->zeros, W->bits, W->group, m, W->k, X, ldx);
-  // mid-batch m (group scales: any m > 32; per tensor: up to 64, past which
-  // the prefill kernel is faster): 32-row chunks on the batched-decode kernel
-  const bool use_chunks = m > 32 && (W->group != 0 || m <= 64) &&
+  // mid-batch m (up to 64, past which the prefill kernel is faster, or any m
+  // > 32 the prefill kernel does not take): 32-row chunks on the
+  // batched-decode kernel
+  const bool use_chunks = m > 32 && (m <= 64 || !zq::gemm_prefill_supported(a)) &&
                           zq::mstream_supported(W->packed, W->scales, W->zeros, W->bits, W->group, 32, W->k, X, ldx);
   if (use_chunks) {
     const int ysz = y_dtype == ZQ_F32 ? 4 : 2;
@@ -397,8 +398,8 @@ zq_status zq_gemm(const zq_weight* W, const void* X, zq_dtype x_dtype, int64_t m
     e = use_stream ? zq::launch_stream_single(p, m, s) : zq::launch_mstream_single(p, m, s);
   } else if (!asym && m <= 4 && aligned16 && zq::gemv_valu_lds_bytes(W->bits, m, W->k) <= 64 * 1024)
     e = zq::launch_gemv_valu(a);
-  else if (!asym && aligned16 && zq::gemm_prefill2_supported(a))
-    e = zq::launch_gemm_prefill2(a);
+  else if (!asym && aligned16 && zq::gemm_prefill_supported(a))
+    e = zq::launch_gemm_prefill(a);
   else if (!asym && aligned16 && zq::gemm_mfma_supported(a))
     e = zq::launch_gemm_mfma(a);
   else
@@ -420,13 +421,15 @@ struct zq_plan_s {
   int variant = 0;  // the kernel variant of the plan's one format, or the mixed-format one
   int grid = 0;     // workgroups of the launch (the ranges table has one entry per segment and workgroup)
   size_t lds = 0;
-  // prefill plans (m > 64): one tile queue per bit width, run in turn
+  // prefill plans (m > 64): one tile queue per bit width and group size, run
+  // in turn
+  static constexpr int PREFILL_KINDS = 6;
   bool prefill = false;
-  zq::PrefillProblem* pprobs = nullptr;  // device, grouped by bit width
+  zq::PrefillProblem* pprobs = nullptr;  // device, grouped by bit width and group size
   int xt = 0;
   int ngroup = 0;
-  int gfirst[3] = {0, 0, 0}, gcount[3] = {0, 0, 0}, gbits[3] = {0, 0, 0};
-  int64_t gtotal[3] = {0, 0, 0};  // tiles
+  int gfirst[PREFILL_KINDS] = {}, gcount[PREFILL_KINDS] = {}, gbits[PREFILL_KINDS] = {}, ggroup[PREFILL_KINDS] = {};
+  int64_t gtotal[PREFILL_KINDS] = {};  // tiles
   // mid-batch plans (32 < m): plans of at most 32 activation rows each, run in turn
   std::vector<zq_plan_s*> chunks;
 };
@@ -453,8 +456,9 @@ void seg_ranges(const zq::StreamPhase& sg, const std::vector<zq::StreamProblem>&
   }
 }
 
-// A prefill plan (m > 64): every product per-tensor scaled, k a multiple of
-// 64, 16-byte aligned codes and activations, one activation type, one phase.
+// A prefill plan (m > 64): every product with symmetric codes, one scale per
+// tensor (k a multiple of 64) or per row and 128 k, 16-byte aligned codes and
+// activations, one activation type, one phase.
 zq_status create_prefill_plan(const zq_problem* problems, int count, int64_t m, zq_plan* plan_out) {
   std::vector<zq::PrefillProblem> pp(count);
   std::vector<int> order(count);
@@ -484,9 +488,9 @@ zq_status create_prefill_plan(const zq_problem* problems, int count, int64_t m, 
     a.x = (const uint16_t*)q.x;
     a.m = m;
     a.ldx = q.ldx;
-    if (!zq::prefill_plan_supported(a))
-      return fail(ZQ_ERR_UNSUPPORTED, "problem %d: prefill plans need one scale per tensor, symmetric codes, k a "
-                  "multiple of 64 and 16-byte aligned codes and activations", i);
+    if (!zq::gemm_prefill_supported(a))
+      return fail(ZQ_ERR_UNSUPPORTED, "problem %d: prefill plans need symmetric codes, k a multiple of 64 (of 128 "
+                  "with group scales) and 16-byte aligned codes and activations", i);
     zq::PrefillProblem& p = pp[i];
     p = zq::PrefillProblem{};
     p.packed = a.packed;
@@ -498,15 +502,18 @@ zq_status create_prefill_plan(const zq_problem* problems, int count, int64_t m, 
     p.k = q.w.k;
     p.ldx = q.ldx;
     p.ldy = q.ldy;
-    p.mtiles = (m + zq::PREFILL_TILE - 1) / zq::PREFILL_TILE;
+    p.mtiles = (m + zq::PREFILL_TILE_M - 1) / zq::PREFILL_TILE_M;
     p.bits = q.w.bits;
+    p.group = q.w.group;
     p.yt = q.y_dtype == ZQ_F32 ? zq::YF32 : q.y_dtype == ZQ_F16 ? zq::YF16 : zq::YBF16;
     order[i] = i;
   }
-  // one queue per bit width (a kernel per width); within it the longest
-  // tiles first, so the last round of the queue is made of short ones
+  // one queue per bit width and group size (a kernel each); within it the
+  // longest tiles first, so the last round of the queue is made of short ones
   std::stable_sort(order.begin(), order.end(), [&](int u, int v) {
-    return pp[u].bits != pp[v].bits ? pp[u].bits < pp[v].bits : pp[u].k > pp[v].k;
+    if (pp[u].bits != pp[v].bits) return pp[u].bits < pp[v].bits;
+    if (pp[u].group != pp[v].group) return pp[u].group < pp[v].group;
+    return pp[u].k > pp[v].k;
   });
   std::vector<zq::PrefillProblem> sorted(count);
   zq_plan_s* plan = new zq_plan_s;
@@ -516,14 +523,15 @@ zq_status create_prefill_plan(const zq_problem* problems, int count, int64_t m, 
   int64_t total = 0;
   for (int i = 0; i < count; ++i) {
     sorted[i] = pp[order[i]];
-    if (i == 0 || sorted[i].bits != sorted[i - 1].bits) {
+    if (i == 0 || sorted[i].bits != sorted[i - 1].bits || sorted[i].group != sorted[i - 1].group) {
       plan->gfirst[plan->ngroup] = i;
       plan->gbits[plan->ngroup] = sorted[i].bits;
+      plan->ggroup[plan->ngroup] = sorted[i].group;
       ++plan->ngroup;
       total = 0;
     }
     sorted[i].tile0 = total;
-    total += sorted[i].mtiles * ((sorted[i].n + zq::PREFILL_TILE - 1) / zq::PREFILL_TILE);
+    total += sorted[i].mtiles * ((sorted[i].n + zq::PREFILL_TILE_N - 1) / zq::PREFILL_TILE_N);
     plan->gcount[plan->ngroup - 1] += 1;
     plan->gtotal[plan->ngroup - 1] = total;
     if (total >= (int64_t)1 << 31) {
@@ -532,7 +540,7 @@ zq_status create_prefill_plan(const zq_problem* problems, int count, int64_t m, 
     }
   }
   hipError_t e = hipMalloc(&plan->pprobs, sizeof(zq::PrefillProblem) * count);
-  const size_t sync_bytes = 3 * zq::PREFILL_SYNC_WORDS * sizeof(uint32_t);
+  const size_t sync_bytes = zq_plan_s::PREFILL_KINDS * zq::PREFILL_SYNC_WORDS * sizeof(uint32_t);
   if (e == hipSuccess) e = hipMalloc(&plan->sync, sync_bytes);
   if (e == hipSuccess)
     e = hipMemcpy(plan->pprobs, sorted.data(), sizeof(zq::PrefillProblem) * count, hipMemcpyHostToDevice);
@@ -549,11 +557,10 @@ zq_status create_prefill_plan(const zq_problem* problems, int count, int64_t m, 
 }  // namespace
 
 namespace {
-// A mid-batch plan (32 < m, INT4 products the MFMA batched-decode kernel
-// takes): the rows go in chunks of 32 (the last one shorter), each chunk a
-// plan of its own over all products; the weights stream once per chunk.
-// Measured on the 7B stack with group scales this beats the tiled MFMA
-// kernels at every m they were tried on (48..512), by 4x to 8x.
+// A mid-batch plan (32 < m <= 64, or asymmetric codes at any m > 32; INT4
+// products the MFMA batched-decode kernel takes): the rows go in chunks of
+// 32 (the last one shorter), each chunk a plan of its own over all products;
+// the weights stream once per chunk.
 zq_status create_chunked_plan(const zq_problem* problems, int count, int64_t m, zq_plan* plan_out) {
   for (int i = 0; i < count; ++i) {
     const zq_problem& q = problems[i];
@@ -561,8 +568,8 @@ zq_status create_chunked_plan(const zq_problem* problems, int count, int64_t m, 
     if (st) return fail(st, "problem %d: %s", i, g_err);
     if (!zq::mstream_supported(q.w.packed, q.w.scales, q.w.zeros, q.w.bits, q.w.group, 32, q.w.k, q.x, q.ldx))
       return fail(ZQ_ERR_UNSUPPORTED, "problem %d: plans with m > 32 need INT4 codes, k a multiple of 512, "
-                  "16-byte aligned codes and activations and 8-byte aligned scales (or, for m > 64, one scale "
-                  "per tensor)", i);
+                  "16-byte aligned codes and activations and 8-byte aligned scales (for m > 64: symmetric "
+                  "codes)", i);
   }
   zq_plan_s* plan = new zq_plan_s;
   plan->m = m;
@@ -598,9 +605,9 @@ zq_status zq_plan_create(const zq_problem* problems, int count, int64_t m, zq_pl
   if (count < 1 || !problems) return fail(ZQ_ERR_INVALID_ARG, "empty problem list");
   if (m < 1) return fail(ZQ_ERR_UNSUPPORTED, "plans take m >= 1 (m=%lld)", (long long)m);
   if (m > 32) {
-    // per-tensor scales and m > 64: the prefill tile queues
+    // symmetric codes and m > 64: the prefill tile queues
     bool prefill = m > 64;
-    for (int i = 0; i < count && prefill; ++i) prefill = problems[i].w.group == 0 && !problems[i].w.zeros;
+    for (int i = 0; i < count && prefill; ++i) prefill = !problems[i].w.zeros;
     if (prefill) return create_prefill_plan(problems, count, m, plan_out);
     return create_chunked_plan(problems, count, m, plan_out);
   }
@@ -797,7 +804,8 @@ zq_status zq_plan_run(zq_plan plan, void* stream) {
     hipError_t e = hipSuccess;
     for (int g = 0; g < plan->ngroup && e == hipSuccess; ++g)
       e = zq::launch_prefill_plan(plan->pprobs + plan->gfirst[g], plan->gcount[g], plan->gtotal[g], plan->xt,
-                                  plan->gbits[g], plan->sync + zq::PREFILL_SYNC_WORDS * g, (hipStream_t)stream);
+                                  plan->gbits[g], plan->ggroup[g], plan->sync + zq::PREFILL_SYNC_WORDS * g,
+                                  (hipStream_t)stream);
     return e == hipSuccess ? ok() : hip_fail(e, "plan launch");
   }
   hipError_t e = plan->mfma

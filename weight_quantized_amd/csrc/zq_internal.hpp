@@ -89,11 +89,13 @@ hipError_t launch_mstream_plan(const StreamPhase* dev_segs, int nseg, const Stre
 // vector-ALU kernel for m <= 4 with x staged in LDS
 size_t gemv_valu_lds_bytes(int bits, int64_t m, int64_t k);
 hipError_t launch_gemv_valu(const GemmArgs& a);
-// prefill MFMA kernel: m > 64, one scale per tensor, k a multiple of 64
-bool gemm_prefill2_supported(const GemmArgs& a);
-hipError_t launch_gemm_prefill2(const GemmArgs& a);
-// One product of a prefill plan (device pointers): its 256 x 256 tiles are
-// plan tiles [tile0, tile0 + mtiles * ntiles), row block fastest.
+// prefill MFMA kernel: m > 64, symmetric codes, one scale per tensor (k a
+// multiple of 64) or per row and 128 k
+bool gemm_prefill_supported(const GemmArgs& a);
+hipError_t launch_gemm_prefill(const GemmArgs& a);
+// One product of a prefill plan (device pointers): its 128 x 256 tiles
+// (PREFILL_TILE_M x PREFILL_TILE_N) are plan tiles [tile0, tile0 + mtiles *
+// ntiles), row block fastest.
 struct PrefillProblem {
   const uint8_t* packed;
   const uint16_t* scales;
@@ -101,16 +103,15 @@ struct PrefillProblem {
   void* y;
   int64_t m, n, k, ldx, ldy;
   int64_t tile0, mtiles;
-  int32_t bits, yt;
+  int32_t bits, yt, group;
 };
-constexpr int PREFILL_TILE = 256;
-bool prefill_plan_supported(const GemmArgs& a);
-// persistent launch over the `total` tiles of products of one bit width;
-// xt: their activations' type; sync: PREFILL_SYNC_WORDS device words (tile
-// counters, finished workgroups), zero before the first run
+constexpr int PREFILL_TILE_M = 128, PREFILL_TILE_N = 256;
+// persistent launch over the `total` tiles of products of one bit width and
+// group size; xt: their activations' type; sync: PREFILL_SYNC_WORDS device
+// words (tile counters, finished workgroups), zero before the first run
 constexpr int PREFILL_SYNC_WORDS = 16;
 hipError_t launch_prefill_plan(const PrefillProblem* dev_probs, int nprob, int64_t total, int xt, int bits,
-                               uint32_t* sync, hipStream_t stream);
+                               int group, uint32_t* sync, hipStream_t stream);
 // MFMA kernels for larger m
 bool gemm_mfma_supported(const GemmArgs& a);
 hipError_t launch_gemm_mfma(const GemmArgs& a);

@@ -1,29 +1,38 @@
 // zq_prefill.hip -- host launchers of the prefill MFMA kernels (m > 64, one
-// scale per tensor); tile and kernels in zq_prefill_impl.hpp.
+// scale per tensor or per row and 128 k); tile and kernels in
+// zq_prefill_impl.hpp.
 #include "zq_prefill_impl.hpp"
 
 namespace zq {
 
-static const void* prefill_fn_for(int bits, int xt, bool plan) {
-  return bits == 2 ? prefill_fn_b2(xt, plan) : bits == 4 ? prefill_fn_b4(xt, plan) : prefill_fn_b8(xt, plan);
+static_assert(PREFILL_TILE_M == PF_BM && PREFILL_TILE_N == PF_BN, "plan tiles are the kernel's");
+
+static const void* prefill_fn_for(int bits, int xt, bool plan, bool gs) {
+  return bits == 2 ? prefill_fn_b2(xt, plan, gs) : bits == 4 ? prefill_fn_b4(xt, plan, gs)
+                                                             : prefill_fn_b8(xt, plan, gs);
 }
 
 // The tile addresses its activations and codes through 32-bit buffer
-// offsets from the tile's first row: 256 rows of either must stay below 4 GB.
-bool gemm_prefill2_supported(const GemmArgs& a) {
-  if (a.group != 0 || a.m <= 64 || a.k % PF_BK != 0 || a.k == 0) return false;
-  if (((uintptr_t)a.x & 15) || ((a.ldx * 2) & 15) || ((uintptr_t)a.packed & 15)) return false;
+// offsets from the tile's first row: 128 rows of activations and 256 rows of
+// codes must stay below 4 GB.
+bool gemm_prefill_supported(const GemmArgs& a) {
+  if (a.zeros != nullptr || a.m <= 64 || a.k == 0) return false;
+  if (a.group == 0 ? a.k % PF_BK != 0 : (a.group != PF_GROUP || a.k % PF_GROUP != 0)) return false;
+  if (((uintptr_t)a.x & 15) || ((a.ldx * 2) & 15) || ((uintptr_t)a.packed & 15) || ((uintptr_t)a.scales & 1))
+    return false;
   if ((int64_t)PF_BM * a.ldx * 2 >= ((int64_t)1 << 32) || (int64_t)PF_BN * a.k * a.bits / 8 >= ((int64_t)1 << 32))
     return false;
   return true;
 }
 
-bool prefill_plan_supported(const GemmArgs& a) { return a.zeros == nullptr && gemm_prefill2_supported(a); }
+static hipError_t set_lds(const void* fn, int lds) {
+  return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+}
 
-hipError_t launch_gemm_prefill2(const GemmArgs& a) {
-  const void* fn = prefill_fn_for(a.bits, a.xt, false);
+hipError_t launch_gemm_prefill(const GemmArgs& a) {
+  const void* fn = prefill_fn_for(a.bits, a.xt, false, a.group != 0);
   const int lds = pf_lds(a.bits);
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  hipError_t e = set_lds(fn, lds);
   if (e != hipSuccess) return e;
   int mtiles = (int)((a.m + PF_BM - 1) / PF_BM);
   const int64_t tiles = (int64_t)mtiles * ((a.n + PF_BN - 1) / PF_BN);
@@ -37,13 +46,14 @@ hipError_t launch_gemm_prefill2(const GemmArgs& a) {
   return hipLaunchKernel(fn, dim3((unsigned)tiles), dim3(256), args, lds, a.stream);
 }
 
+// two workgroups per CU stay resident (LDS and registers are sized for it)
 hipError_t launch_prefill_plan(const PrefillProblem* dev_probs, int nprob, int64_t total, int xt, int bits,
-                               uint32_t* sync, hipStream_t stream) {
-  const void* fn = prefill_fn_for(bits, xt, true);
+                               int group, uint32_t* sync, hipStream_t stream) {
+  const void* fn = prefill_fn_for(bits, xt, true, group != 0);
   const int lds = pf_lds(bits);
-  hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, lds);
+  hipError_t e = set_lds(fn, lds);
   if (e != hipSuccess) return e;
-  const int64_t G = std::min<int64_t>(stream_grid(), total);
+  const int64_t G = std::min<int64_t>(2 * (int64_t)stream_grid(), total);
   void* args[] = {(void*)&dev_probs, &nprob, &total, &sync};
   return hipLaunchKernel(fn, dim3((unsigned)G), dim3(256), args, lds, stream);
 }
