@@ -15,13 +15,17 @@ other workloads of the pages' benchmark set and adds each as a key of its own
 (each with its roofline fraction; --no-extras skips them):
   config1_gemv512        the 512 x 512 INT4 GEMV (latency: us per call)
   config3_batch          the 7B stack's weights at M = 1, 4, 8, 16, 32 bf16 rows
+  mid_batch_prefill      the same weights at M = 128, 256, 512 (prefill tiles),
+                         beside the stack with one scale per tensor
   config4_qwen32b_decode the Qwen2.5-32B-shaped decode stack, M = 1
   config5_prefill        the mixed INT2/4/8 prefill stack, M = 2048 (TFLOP/s)
 
 Other workloads (--config) print their own line:
   gemv-512             single 512 x 512 INT4 GEMV, per-tensor scale fp16(0.02)
   qwen7b-batch --m M   the 7B stack at M rows of bf16 activations (M <= 32: one
-                       plan launch; M > 32: 32-row chunks of it)
+                       plan launch; 32 < M <= 64: 32-row chunks of it; M > 64:
+                       prefill tiles)
+  qwen7b-batch-tensor --m M   the same shapes, INT4 with one scale per tensor
   qwen32b-decode       64 layers of Qwen2.5-32B projection shapes, M = 1
   qwen7b-decode-asym   the 7B decode stack with asymmetric INT4 weights (unsigned
                        codes, fp16 scale and zero point per 128-group)
@@ -80,8 +84,8 @@ def parse():
     p.add_argument("--steps", type=int, default=50)
     p.add_argument("--warmup", type=int, default=5)
     p.add_argument("--config", default="qwen7b-decode",
-                   choices=["gemv-512", "qwen7b-decode", "qwen7b-batch", "qwen32b-decode", "qwen7b-prefill",
-                            "qwen7b-decode-asym", "qwen7b-decode-tp4", "hbm-copy"])
+                   choices=["gemv-512", "qwen7b-decode", "qwen7b-batch", "qwen7b-batch-tensor", "qwen32b-decode",
+                            "qwen7b-prefill", "qwen7b-decode-asym", "qwen7b-decode-tp4", "hbm-copy"])
     p.add_argument("--m", type=int, default=None, help="activation rows (qwen7b-batch)")
     p.add_argument("--launch", default=None, choices=["plan", "graph", "eager"],
                    help="plan (the default): one resident launch per step (m <= 32), or one "
@@ -116,6 +120,8 @@ class Stack:
             shapes, L, bits_of, group, xdt, self.m = synth.QWEN25_7B_TP4, 28, (lambda l: 4), 128, "f16", 1
         elif cfg == "qwen7b-batch":
             shapes, L, bits_of, group, xdt, self.m = synth.QWEN25_7B, 28, (lambda l: 4), 128, "bf16", m or 8
+        elif cfg == "qwen7b-batch-tensor":  # the same shapes, INT4 with one scale per tensor
+            shapes, L, bits_of, group, xdt, self.m = synth.QWEN25_7B, 28, (lambda l: 4), 0, "bf16", m or 128
         elif cfg == "qwen32b-decode":
             shapes, L, bits_of, group, xdt, self.m = synth.QWEN25_32B, 64, (lambda l: 4), 128, "f16", 1
         else:
@@ -448,6 +454,28 @@ def extras(a, base: Stack, torch, zq, synth) -> dict:
     out["config3_batch"] = {"workload": "Qwen2.5-7B-shaped stack (config 2's weights), INT4 group-128, bf16 x, "
                                         "one plan per M", "by_m": batch}
     torch.cuda.empty_cache()
+    # past 64 rows (prefill tiles): config 2's group-128 weights beside the
+    # same stack with one scale per tensor
+    mid = {}
+    pt = Stack("qwen7b-batch-tensor", 128, None, torch, zq, synth)
+    for m in (128, 256, 512):
+        row = {}
+        for kind, src in (("group128", base), ("per_tensor", pt)):
+            st = src.with_rows(m, "bf16")
+            st.make_plan("independent")
+            t = measure(st.plan_step, 20, 3, torch, settle_s=0.05)
+            f = prefill_figures(st, t, t["ms_mean_of_steps"])
+            row[kind] = {k: f[k] for k in ("value", "unit", "mfma_frac", "us_per_layer", "ms_per_step_median")}
+            st.close()
+            del st
+        row["group_over_tensor_time"] = round(row["group128"]["us_per_layer"] / row["per_tensor"]["us_per_layer"], 4)
+        mid[f"m{m}"] = row
+    pt.close()
+    del pt
+    out["mid_batch_prefill"] = {"workload": "Qwen2.5-7B-shaped stack, INT4, bf16 x, one prefill plan per M: "
+                                            "group-128 scales (config 2's weights) and one scale per tensor",
+                                "by_m": mid}
+    torch.cuda.empty_cache()
     # config 4: the 32B stack (16.09 GB of weights)
     st = Stack("qwen32b-decode", None, None, torch, zq, synth)
     st.make_plan("independent")
@@ -564,14 +592,16 @@ def main():
         "qwen7b-decode-tp4": "one rank's 4-way tensor-parallel shard of the Qwen2.5-7B decode stack: 28 layers "
                              "x 7 projections, M=1, INT4 group-128, fp16 x",
         "qwen7b-batch": f"Qwen2.5-7B-shaped stack, M={stack.m}, INT4 group-128, bf16 x",
+        "qwen7b-batch-tensor": f"Qwen2.5-7B-shaped stack, M={stack.m}, INT4 one scale per tensor, bf16 x",
         "qwen32b-decode": "Qwen2.5-32B-shaped decode stack: 64 layers x 7 projections, M=1, INT4 group-128, fp16 x",
         "qwen7b-prefill": "Qwen2.5-7B-shaped prefill stack, per-layer INT2/INT4/INT8, per-tensor scale, M=2048, bf16 x",
     }[a.config], "layers": stack.layers, "m": stack.m,
         "weight_bytes_per_step": stack.weight_bytes, "launch": a.launch, "order": a.order if a.launch == "plan" else "stream",
         "launches_per_step": 1 if a.launch == "plan" else len(stack.launches),
-        # kernels one plan run enqueues: one per bit width (prefill tile
-        # queues), one per 32-row chunk (m > 32 on the batched-decode kernel)
-        "kernels_per_plan_run": (len({W.bits for W, _, _ in stack.launches}) if stack.m > 64 and stack.group == 0
+        # kernels one plan run enqueues: one per bit width and scale kind
+        # (prefill tile queues), one per 32-row chunk (32 < m <= 64 on the
+        # batched-decode kernel)
+        "kernels_per_plan_run": (len({(W.bits, W.group) for W, _, _ in stack.launches}) if stack.m > 64
                                  else -(-stack.m // 32) if stack.m > 32 else 1) if a.launch == "plan" else None,
         "wall_ms_per_step": round(t["wall_ms"], 5), "avg_kernel_us": round(avg_launch_ms * 1e3, 3),
         "streams": a.streams if a.launch == "graph" else 1,

@@ -65,7 +65,15 @@
 extern "C" {
 #endif
 
-typedef enum {
+/* In C++ the enums below have int as their underlying type, so that any int
+ * a C caller passes is a valid value to validate (C enums are ints). */
+#ifdef __cplusplus
+#define ZQ_ENUM_BASE : int
+#else
+#define ZQ_ENUM_BASE
+#endif
+
+typedef enum ZQ_ENUM_BASE {
   ZQ_OK = 0,
   ZQ_ERR_INVALID_ARG = 1,
   ZQ_ERR_UNSUPPORTED = 2,
@@ -73,7 +81,7 @@ typedef enum {
   ZQ_ERR_HIP = 4
 } zq_status;
 
-typedef enum {
+typedef enum ZQ_ENUM_BASE {
   ZQ_I8 = 0,   /* int8 integer codes */
   ZQ_F16 = 1,  /* IEEE binary16 */
   ZQ_BF16 = 2, /* bfloat16 */
@@ -95,11 +103,16 @@ typedef struct zq_weight {
                            * bits 2 or 4 and group 128 only. */
 } zq_weight;
 
-/* Bytes of packed codes: n * k * bits / 8. Returns 0 for unsupported bits. */
+/* Bytes of packed codes: n * k * bits / 8. Returns 0 for unsupported bits.
+ * [wiki, section "Формат модели .zse": two INT4 values per byte; zQuantize
+ * (openclawradar, section "Componentes da arquitetura") stores INT2 and INT8
+ * tensors the same way, 4 and 1 codes per byte.] */
 size_t zq_packed_bytes(int bits, int64_t n, int64_t k);
 
 /* Number of fp16 scales: 1 for group 0, n * (k / 128) for group 128;
- * -1 for an unsupported group. */
+ * -1 for an unsupported group. [wiki, section "Формат модели .zse": one fp16
+ * scale per group of 128 weights; zQuantize's per-tensor variant: one per
+ * tensor.] */
 int64_t zq_num_scales(int group, int64_t n, int64_t k);
 
 /*
@@ -310,10 +323,14 @@ zq_status zq_plan_run(zq_plan plan, void* stream);
 zq_status zq_plan_check(zq_plan plan);
 zq_status zq_plan_destroy(zq_plan plan);
 
-/* Static description of a status code. */
+/* Static description of a status code. The pages define no error
+ * interface: the status codes and these two calls are this library's own
+ * (the problem statement's calls -- zq_pack, zq_gemv, zq_gemm -- report
+ * through them). */
 const char* zq_status_string(zq_status s);
 
-/* Detail of the last failed call made by this thread ("" if none). */
+/* Detail of the last failed call made by this thread ("" if none); see
+ * zq_status_string. */
 const char* zq_last_error(void);
 
 #ifdef __cplusplus

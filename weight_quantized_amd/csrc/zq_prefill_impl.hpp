@@ -329,7 +329,8 @@ __device__ __forceinline__ void pf_tile_w(const uint8_t* __restrict__ packed, co
     for (int j = 0; j < FJ; ++j) {
       const float s = f16_bits_to_float(s16[j]) * D::F;
       const bool nz = s != 0.f;
-      rat[j] = nz ? u[j] / s : 1.f;
+      // ratio through the hardware reciprocal (1 ulp; exact for powers of 2)
+      rat[j] = nz ? u[j] * __builtin_amdgcn_rcpf(s) : 1.f;
       u[j] = nz ? s : u[j];
       kn[j] = D::key(nz ? 0xFFFFFFFFu : 0u);
     }
