@@ -14,7 +14,8 @@ static const void* prefill_fn_for(int bits, int xt, bool plan, bool gs) {
 
 // The tile addresses its activations and codes through 32-bit buffer
 // offsets from the tile's first row: 128 rows of activations and 256 rows of
-// codes must stay below 4 GB.
+// codes must stay below 4 GB. A single call's grid is (row blocks, column
+// blocks): at most 65535 column blocks.
 bool gemm_prefill_supported(const GemmArgs& a) {
   if (a.zeros != nullptr || a.m <= 64 || a.k == 0) return false;
   if (a.group == 0 ? a.k % PF_BK != 0 : (a.group != PF_GROUP || a.k % PF_GROUP != 0)) return false;
@@ -22,7 +23,7 @@ bool gemm_prefill_supported(const GemmArgs& a) {
     return false;
   if ((int64_t)PF_BM * a.ldx * 2 >= ((int64_t)1 << 32) || (int64_t)PF_BN * a.k * a.bits / 8 >= ((int64_t)1 << 32))
     return false;
-  return true;
+  return (a.n + PF_BN - 1) / PF_BN <= 65535 && (a.m + PF_BM - 1) / PF_BM < ((int64_t)1 << 31);
 }
 
 static hipError_t set_lds(const void* fn, int lds) {
@@ -34,16 +35,15 @@ hipError_t launch_gemm_prefill(const GemmArgs& a) {
   const int lds = pf_lds(a.bits);
   hipError_t e = set_lds(fn, lds);
   if (e != hipSuccess) return e;
-  int mtiles = (int)((a.m + PF_BM - 1) / PF_BM);
-  const int64_t tiles = (int64_t)mtiles * ((a.n + PF_BN - 1) / PF_BN);
+  const int64_t mtiles = (a.m + PF_BM - 1) / PF_BM, ntiles = (a.n + PF_BN - 1) / PF_BN;
   const uint8_t* packed = a.packed;
   const uint16_t* scales = a.scales;
   int64_t n = a.n, k = a.k, m = a.m, ldx = a.ldx, ldy = a.ldy;
   const uint16_t* x = a.x;
   void* y = a.y;
   int yt = a.yt;
-  void* args[] = {&packed, &scales, &n, &k, &x, &m, &ldx, &y, &ldy, &yt, &mtiles};
-  return hipLaunchKernel(fn, dim3((unsigned)tiles), dim3(256), args, lds, a.stream);
+  void* args[] = {&packed, &scales, &n, &k, &x, &m, &ldx, &y, &ldy, &yt};
+  return hipLaunchKernel(fn, dim3((unsigned)mtiles, (unsigned)ntiles), dim3(256), args, lds, a.stream);
 }
 
 // two workgroups per CU stay resident (LDS and registers are sized for it)

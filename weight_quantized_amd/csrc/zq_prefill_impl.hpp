@@ -132,6 +132,98 @@ __device__ __forceinline__ uint32_t pf_h2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, h2{(_Float16)lo, (_Float16)hi});
 }
 
+// Magic-number decode (one scale per tensor): the 8 codes k0..k7 of one MFMA
+// step become 4 dwords of 16-bit pairs (k 2j, 2j+1) = (q + BE, q + BO),
+// exact; the offsets times the activations' row sums are removed in the
+// epilogue. Pairs are built by
+// one v_perm_b32 (the code byte copied to bytes 0 and 2, zeros elsewhere)
+// and one and-xor (v_bitop3): the field mask, the sign flip and the magic
+// exponent. The two halves may use different magic numbers.
+template <int XT, int BITS>
+struct PfMagic;
+
+// INT4. bf16: both nibbles at fraction bits 3:0 under 128 (v >> 4 brings
+// the odd nibble down): 136 + q. fp16: even nibble at bits 3:0 under 1024,
+// odd nibble left at bits 7:4 under 64: 1032 + q, 72 + q; no shift.
+template <int XT>
+struct PfMagic<XT, 4> {
+  static constexpr float BE = XT == XBF16 ? 136.f : 1032.f, BO = XT == XBF16 ? 136.f : 72.f;
+  static constexpr uint32_t BW = XT == XBF16 ? 0x43084308u : 0x54806408u;  // (BE, BO) as a 16-bit pair
+  static __device__ __forceinline__ u4 frag(const u4 (&c)[2], int kk) {
+    const uint32_t v = c[0][kk];
+    if constexpr (XT == XBF16) {
+      const uint32_t s = v >> 4;
+      return u4{(__builtin_amdgcn_perm(s, v, 0x0C040C00u) & 0x000F000Fu) ^ 0x43084308u,
+                (__builtin_amdgcn_perm(s, v, 0x0C050C01u) & 0x000F000Fu) ^ 0x43084308u,
+                (__builtin_amdgcn_perm(s, v, 0x0C060C02u) & 0x000F000Fu) ^ 0x43084308u,
+                (__builtin_amdgcn_perm(s, v, 0x0C070C03u) & 0x000F000Fu) ^ 0x43084308u};
+    } else {
+      return u4{(__builtin_amdgcn_perm(v, v, 0x0C000C00u) & 0x00F0000Fu) ^ 0x54806408u,
+                (__builtin_amdgcn_perm(v, v, 0x0C010C01u) & 0x00F0000Fu) ^ 0x54806408u,
+                (__builtin_amdgcn_perm(v, v, 0x0C020C02u) & 0x00F0000Fu) ^ 0x54806408u,
+                (__builtin_amdgcn_perm(v, v, 0x0C030C03u) & 0x00F0000Fu) ^ 0x54806408u};
+    }
+  }
+};
+
+// INT2: a byte holds codes 4j..4j+3 at bits 1:0, 3:2, 5:4, 7:6.
+// bf16: even codes at fraction bits 1:0 under 128, odd codes at bits 3:2 of
+// the upper half under 32 (v >> 4 serves the upper two codes of each byte):
+// 130 + q, 34 + q. fp16: every code at fraction bits 9:8 under 4 (the byte
+// moved to the upper byte of its half, the sources shifted by 0, 2, 4, 6):
+// 6 + q for both halves -- a small offset, so that the fp32 sums of long rows
+// carry little of it.
+template <int XT>
+struct PfMagic<XT, 2> {
+  static constexpr float BE = XT == XBF16 ? 130.f : 6.f, BO = XT == XBF16 ? 34.f : 6.f;
+  static constexpr uint32_t BW = XT == XBF16 ? 0x42084302u : 0x46004600u;
+  static __device__ __forceinline__ u4 frag(const u4 (&c)[2], int kk) {
+    const uint32_t v = c[0][kk >> 1];
+    // bytes 2(kk&1) and 2(kk&1)+1 of the dword hold this step's 8 codes
+    const uint32_t j0 = 2 * (kk & 1), j1 = j0 + 1;
+    if constexpr (XT == XBF16) {
+      constexpr uint32_t M = 0x000C0003u, K = 0x42084302u;  // field masks; exponents | sign flips
+      const uint32_t s = v >> 4;
+      auto pr = [&](uint32_t src, uint32_t j) __attribute__((always_inline)) {
+        return (__builtin_amdgcn_perm(src, src, 0x0C000C00u | (j << 16) | j) & M) ^ K;
+      };
+      return u4{pr(v, j0), pr(s, j0), pr(v, j1), pr(s, j1)};
+    } else {
+      constexpr uint32_t M = 0x03000300u, K = 0x46004600u;
+      auto pr = [&](uint32_t lo, uint32_t hi, uint32_t j) __attribute__((always_inline)) {
+        return (__builtin_amdgcn_perm(hi, lo, 0x000C000Cu | ((4 + j) << 24) | (j << 8)) & M) ^ K;
+      };
+      const uint32_t v2 = v >> 2, v4 = v >> 4, v6 = v >> 6;
+      return u4{pr(v, v2, j0), pr(v4, v6, j0), pr(v, v2, j1), pr(v4, v6, j1)};
+    }
+  }
+};
+
+// INT8. bf16: u = q + 128 (sign flip) converted to float exactly, upper
+// halves joined: 128 + q. fp16: the flipped byte in fraction bits 7:0 under
+// 1024: 1152 + q, one v_perm and one xor per pair.
+template <int XT>
+struct PfMagic<XT, 8> {
+  static constexpr float BE = XT == XBF16 ? 128.f : 1152.f, BO = BE;
+  static constexpr uint32_t BW = XT == XBF16 ? 0x43004300u : 0x64806480u;
+  static __device__ __forceinline__ u4 frag(const u4 (&c)[2], int kk) {
+    const uint32_t v0 = c[kk >> 1][2 * (kk & 1)], v1 = c[kk >> 1][2 * (kk & 1) + 1];
+    if constexpr (XT == XBF16) {
+      auto pr = [](uint32_t v, int i) __attribute__((always_inline)) {
+        const uint32_t f = v ^ 0x80808080u;
+        const float lo = (float)((f >> (16 * i)) & 0xFFu), hi = (float)((f >> (16 * i + 8)) & 0xFFu);
+        return __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
+      };
+      return u4{pr(v0, 0), pr(v0, 1), pr(v1, 0), pr(v1, 1)};
+    } else {
+      return u4{__builtin_amdgcn_perm(v0, v0, 0x0C010C00u) ^ 0x64806480u,
+                __builtin_amdgcn_perm(v0, v0, 0x0C030C02u) ^ 0x64806480u,
+                __builtin_amdgcn_perm(v1, v1, 0x0C010C00u) ^ 0x64806480u,
+                __builtin_amdgcn_perm(v1, v1, 0x0C030C02u) ^ 0x64806480u};
+    }
+  }
+};
+
 // Exact decoders: frag(c, kk, key) gives the 8 codes of MFMA k-step kk as 4
 // dwords of 16-bit pairs (k 2d, 2d + 1) = F^-1 * (q, q'), all zero where the
 // key was made from a zero mask. Code layout as in PfDec.
@@ -240,6 +332,11 @@ __device__ __forceinline__ void pf_tile_w(const uint8_t* __restrict__ packed, co
                                         int64_t n0, uint8_t* smem) {
   using D = PfDec<XT, BITS>;
   using Key = typename D::Key;
+  // one scale per tensor: the magic-number decode, its offsets removed in the
+  // epilogue with the activations' row sums (bf16 INT8 decodes exactly at
+  // the same cost); group scales: the exact decode
+  constexpr bool MAGIC = !GS && !(XT == XBF16 && BITS == 8);
+  using MG = PfMagic<XT, BITS>;
   constexpr int FI = 4, FJ = 2, NS = PF_NS, CR = pf_cr(BITS), CST = pf_cstage(BITS);
   constexpr int CB = 8 * BITS;  // code bytes of one row per 64-k step
   constexpr int NCL = BITS == 8 ? 2 : 1;
@@ -327,8 +424,9 @@ __device__ __forceinline__ void pf_tile_w(const uint8_t* __restrict__ packed, co
   auto next_units = [&](const uint16_t (&s16)[FJ]) __attribute__((always_inline)) {
 #pragma unroll
     for (int j = 0; j < FJ; ++j) {
-      const float s = f16_bits_to_float(s16[j]) * D::F;
-      const bool nz = s != 0.f;
+      const float s = f16_bits_to_float(s16[j]) * (MAGIC ? 1.f : D::F);
+      // one scale per tensor: y = s * acc, whatever s is
+      const bool nz = !GS || s != 0.f;
       // ratio through the hardware reciprocal (1 ulp; exact for powers of 2)
       rat[j] = nz ? u[j] * __builtin_amdgcn_rcpf(s) : 1.f;
       u[j] = nz ? s : u[j];
@@ -355,7 +453,24 @@ __device__ __forceinline__ void pf_tile_w(const uint8_t* __restrict__ packed, co
   };
   auto decode = [&](const u4 (&cb)[FJ][2], int kk, const Key (&key)[FJ], u4 (&b)[FJ]) __attribute__((always_inline)) {
 #pragma unroll
-    for (int j = 0; j < FJ; ++j) b[j] = D::frag(cb[j], kk, key[j]);
+    for (int j = 0; j < FJ; ++j) {
+      if constexpr (MAGIC) b[j] = MG::frag(cb[j], kk);
+      else b[j] = D::frag(cb[j], kk, key[j]);
+    }
+  };
+  // ---- row sums for the magic decode's offsets: in k-step kk the wave sums
+  // the fragment of row tile (kk + W) & 3 it has in registers for its MFMAs
+  // (every row tile and k-step once over the four waves); bs[r]: rows
+  // 32r + l32, k-half g. The four waves' partials are added at the end.
+  float bs[FI];
+#pragma unroll
+  for (int i = 0; i < FI; ++i) bs[i] = 0.f;
+  auto bias_sum = [&](const u4 (&a)[FI], int kk) __attribute__((always_inline)) {
+    if constexpr (MAGIC) {
+      const int r = (kk + W) & 3;
+#pragma unroll
+      for (int d = 0; d < 4; ++d) bs[r] = dot2<XT>(a[r][d], MG::BW, bs[r]);
+    }
   };
   auto rescale = [&]() __attribute__((always_inline)) {
 #pragma unroll
@@ -363,7 +478,8 @@ __device__ __forceinline__ void pf_tile_w(const uint8_t* __restrict__ packed, co
 #pragma unroll
       for (int j = 0; j < FJ; ++j) acc[i][j] *= rat[j];
   };
-  constexpr int DEC_VALU = XT == XF16 ? 26 : BITS == 2 ? 38 : 30;  // decode of one k-step (both fragments)
+  // decode of one k-step (both fragments) and its row sums
+  constexpr int DEC_VALU = MAGIC ? 22 : XT == XF16 ? 26 : BITS == 2 ? 38 : 30;
 
   u4 a0[FI], a1[FI], b0[FJ], b1[FJ];
   u4 cb[FJ][2], ncb[FJ][2];
@@ -419,12 +535,14 @@ __device__ __forceinline__ void pf_tile_w(const uint8_t* __restrict__ packed, co
     if constexpr (GS && !ODD) rescale();
     read_a(cur, 1, a1);
     decode(cb, 1, kc, b1);
+    bias_sum(a0, 0);
     mfmas(a0, b0);
     pf_interleave<FI * FJ, DEC_VALU + (GS && !ODD ? FI * FJ * 16 : 0), FI, VM_EARLY>();
     __builtin_amdgcn_sched_barrier(0);
     // k-step 1
     read_a(cur, 2, a0);
     decode(cb, 2, kc, b0);
+    bias_sum(a1, 1);
     mfmas(a1, b1);
     pf_interleave<FI * FJ, DEC_VALU, FI, 0>();
     __builtin_amdgcn_sched_barrier(0);
@@ -438,6 +556,7 @@ __device__ __forceinline__ void pf_tile_w(const uint8_t* __restrict__ packed, co
     decode(cb, 3, kc, b1);
     read_codes(kt + 1, ncb);
     if constexpr (GS && ODD) next_units(s16);
+    bias_sum(a0, 2);
     mfmas(a0, b0);
     pf_interleave<FI * FJ, DEC_VALU + (GS && ODD ? 24 : 0), FI + (BITS == 2 ? FJ : FJ * NCL), XDMA>();
     __builtin_amdgcn_sched_barrier(0);
@@ -445,6 +564,7 @@ __device__ __forceinline__ void pf_tile_w(const uint8_t* __restrict__ packed, co
     read_a(nxt, 0, a0);
     if constexpr (GS && ODD) decode(ncb, 0, kn, b0);
     else decode(ncb, 0, kc, b0);
+    bias_sum(a1, 3);
     mfmas(a1, b1);
     pf_interleave<FI * FJ, DEC_VALU, FI, 0>();
     __builtin_amdgcn_sched_barrier(0);
@@ -461,20 +581,44 @@ __device__ __forceinline__ void pf_tile_w(const uint8_t* __restrict__ packed, co
   }
   if (!GS && (KT & 1)) step.template operator()<0>(KT - 1);  // one scale: k a multiple of 64 only
 
-  // ---- epilogue: every load done; y = units * acc
+  // ---- epilogue: every load done and every wave past the loop; y = units *
+  // acc (less the scaled offset sums of the row with the magic decode:
+  // partials of the two k-halves added, then those of the four waves, in
+  // LDS: [wave][row], then the total of row t by thread t)
   pf_barrier<0>();
+  const float* sb = reinterpret_cast<const float*>(smem + 4 * PF_BM * 4);
+  if constexpr (MAGIC) {
+    float* sbw = reinterpret_cast<float*>(smem);
+#pragma unroll
+    for (int i = 0; i < FI; ++i) {
+      const float v = bs[i] + __shfl_xor(bs[i], 32, 64);
+      if (g == 0) sbw[w * PF_BM + 32 * i + l32] = v;
+    }
+    __syncthreads();
+    if (tid < PF_BM)
+      reinterpret_cast<float*>(smem + 4 * PF_BM * 4)[tid] =
+          u[0] * (sbw[tid] + sbw[PF_BM + tid] + sbw[2 * PF_BM + tid] + sbw[3 * PF_BM + tid]);
+    __syncthreads();
+  }
   auto epi = [&]<int YT, bool EDGE>() __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < FI; ++i) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
+        // D layout of 32x32: value r of lane l is row 8*(r/4) + 4*(l/32) + r%4,
+        // column l%32
+        const int rl = 32 * i + 8 * q + 4 * g;
+        f4 c4 = f4{};
+        if constexpr (MAGIC) c4 = *reinterpret_cast<const f4*>(sb + rl);
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          const int64_t row = m0 + 32 * i + 8 * q + 4 * g + rr;
+          const int64_t row = m0 + rl + rr;
 #pragma unroll
           for (int j = 0; j < FJ; ++j) {
             const int64_t col = n0 + 64 * w + 32 * j + l32;
-            const float v = u[j] * acc[i][j][4 * q + rr];
+            float v;
+            if constexpr (MAGIC) v = __builtin_fmaf(u[j], acc[i][j][4 * q + rr], -c4[rr]);
+            else v = u[j] * acc[i][j][4 * q + rr];
             if (!EDGE || (row < m && col < n)) store_y(y, row * ldy + col, v, YT);
           }
         }
@@ -508,19 +652,18 @@ __device__ __forceinline__ void pf_tile(const uint8_t* __restrict__ packed, cons
   }
 }
 
-// Single call: one tile per workgroup. Tile i takes row block i % mtiles and
-// column block i / mtiles, so the row blocks of consecutive workgroups --
-// which the hardware deals out to the 8 XCDs in turn -- keep their
-// activation rows within one XCD's L2 when mtiles is a multiple of 8.
+// Single call: one tile per workgroup, grid (row blocks, column blocks). The
+// hardware dispatches workgroups x-fastest and deals them out to the 8 XCDs
+// in turn, so consecutive row blocks of one column block keep their
+// activation rows within one XCD's L2 when there are 8k row blocks.
 template <int XT, int BITS, bool GS>
 __global__ __launch_bounds__(256, 2) void prefill_kernel(const uint8_t* __restrict__ packed,
                                                          const uint16_t* __restrict__ scales, int64_t n, int64_t k,
                                                          const uint16_t* __restrict__ x, int64_t m, int64_t ldx,
-                                                         void* __restrict__ y, int64_t ldy, int yt, int mtiles) {
+                                                         void* __restrict__ y, int64_t ldy, int yt) {
   extern __shared__ __align__(16) uint8_t smem[];
-  const int t = blockIdx.x, mb = t % mtiles, nb = t / mtiles;
-  pf_tile<XT, BITS, GS>(packed, scales, n, k, x, m, ldx, y, ldy, yt, (int64_t)mb * PF_BM, (int64_t)nb * PF_BN,
-                        smem);
+  pf_tile<XT, BITS, GS>(packed, scales, n, k, x, m, ldx, y, ldy, yt, (int64_t)blockIdx.x * PF_BM,
+                        (int64_t)blockIdx.y * PF_BN, smem);
 }
 
 // Prefill plan: the tiles of many products of one bit width and scale kind
@@ -540,10 +683,14 @@ template <int XT, int BITS, bool GS>
 __global__ __launch_bounds__(256, 2) void prefill_plan_kernel(const PrefillProblem* __restrict__ probs, int nprob,
                                                               int64_t total, uint32_t* __restrict__ sync) {
   extern __shared__ __align__(16) uint8_t smem[];
-  // the tile index and its product pass through the first 8 bytes of the
-  // LDS, which no tile uses before the barrier that follows their reading
+  // the tile, its product and its row and column blocks pass through the
+  // first 16 bytes of the LDS, which no tile uses before the barrier that
+  // follows their reading (loads from LDS read into scalar registers keep
+  // the tile's addressing scalar)
   int* s_tile = reinterpret_cast<int*>(smem);  // tiles of one plan stay below 2^31
   int* s_prob = s_tile + 1;
+  int* s_mb = s_tile + 2;
+  int* s_nb = s_tile + 3;
   const int xcc = (int)(__builtin_amdgcn_s_getreg((3 << 11) | 20) & (PP_QUEUES - 1));  // HW_REG_XCC_ID
   int q = 0;  // queues tried so far, starting with this XCD's
   for (;;) {
@@ -556,7 +703,7 @@ __global__ __launch_bounds__(256, 2) void prefill_plan_kernel(const PrefillProbl
         if (t < total) break;
         ++q;  // this queue is empty
       }
-      int p = 0;
+      int p = 0, mb = 0, nb = 0;
       if (t < total) {
         int lo = 0, hi = nprob - 1;  // last product whose first tile is <= t
         while (lo < hi) {
@@ -565,20 +712,24 @@ __global__ __launch_bounds__(256, 2) void prefill_plan_kernel(const PrefillProbl
           else hi = mid - 1;
         }
         p = lo;
+        const int local = (int)(t - probs[p].tile0), mt = (int)probs[p].mtiles;
+        nb = local / mt;
+        mb = local - nb * mt;
       }
       *s_tile = (int)(t < total ? t : total);
       *s_prob = p;
+      *s_mb = mb;
+      *s_nb = nb;
     }
     __syncthreads();
     // uniform values: read into scalar registers, so the tile's addressing
     // stays scalar
     const int64_t t = (int64_t)__builtin_amdgcn_readfirstlane(*s_tile);
     const int pi = __builtin_amdgcn_readfirstlane(*s_prob);
+    const int mb = __builtin_amdgcn_readfirstlane(*s_mb), nb = __builtin_amdgcn_readfirstlane(*s_nb);
     __syncthreads();  // read before the tile's loads and thread 0's next tile
     if (t >= total) break;
     const PrefillProblem& pr = probs[pi];
-    const int local = (int)(t - pr.tile0), mt = (int)pr.mtiles;
-    const int nb = local / mt, mb = local - nb * mt;
     pf_tile<XT, BITS, GS>(pr.packed, pr.scales, pr.n, pr.k, pr.x, pr.m, pr.ldx, pr.y, pr.ldy, pr.yt,
                           (int64_t)mb * PF_BM, (int64_t)nb * PF_BN, smem);
   }
