@@ -237,12 +237,13 @@ zq_status zq_gemv(const zq_weight* W, const void* x, zq_dtype x_dtype, void* y,
  *   m = 2..32, INT4, k a multiple of 512, 16-byte aligned codes and
  *     activations, 8-byte aligned scales (and zero points): a resident MFMA
  *     kernel that streams the codes once;
- *   32 < m <= 64 (or asymmetric codes at m > 32), INT4, k a multiple of
- *     512, aligned as above: that kernel on chunks of 32 rows;
- *   m > 64, symmetric codes, one scale per tensor (k a multiple of 64) or
- *     per row and 128 k, 16-byte aligned codes and activations: a tiled MFMA
- *     kernel (128 x 256 tiles) that decodes codes in registers and applies
- *     group scales in fp32;
+ *   m > 32 (or 16 < m <= 32 in a format the kernel above does not take),
+ *     symmetric codes, one scale per tensor (k a multiple of 64) or per row
+ *     and 128 k, 16-byte aligned codes and activations: a tiled MFMA kernel
+ *     (32, 64 or 128 x 256 tiles for m <= 32, <= 64 and above) that decodes
+ *     codes in registers and applies group scales in fp32;
+ *   asymmetric codes at m > 32, INT4, k a multiple of 512, aligned as
+ *     above: the batched-decode kernel on chunks of 32 rows;
  *   anything else: tiled MFMA kernels, or a general kernel for unaligned and
  *     odd shapes.
  * Codes are decoded to bf16 / fp16 values that are exact for every code.
@@ -271,15 +272,17 @@ zq_status zq_gemm(const zq_weight* W, const void* X, zq_dtype x_dtype, int64_t m
  *              sit in the phase), split evenly over the workgroups.
  * zq_plan_create  validates every problem (as zq_gemm does) and requires
  *              m >= 1 (ZQ_ERR_UNSUPPORTED otherwise).
- *              m > 64 and every problem with symmetric codes (prefill): one
- *              scale per tensor (k a multiple of 64) or per row and 128 k,
- *              16-byte aligned codes and activations, one x dtype and one
- *              phase; the plan runs one persistent launch per bit width and
- *              scale kind present, whose workgroups take 128 x 256 output
- *              tiles from per-XCD device counters, so one run leaves no
- *              launch gaps between products and no idle CUs until its last
- *              round. Results are those of zq_gemm, bit for bit. Other
- *              plans with 32 < m: every problem INT4, k a multiple of 512,
+ *              m > 64 and every problem with symmetric codes, or 32 < m <=
+ *              64 (16 < m <= 32 when some problem is not one the MFMA kernel
+ *              below takes) and every problem one the prefill kernel takes,
+ *              in one phase (prefill): one scale per tensor (k a multiple of 64) or
+ *              per row and 128 k, 16-byte aligned codes and activations, one
+ *              x dtype and one phase; the plan runs one persistent launch per
+ *              bit width and scale kind present, whose workgroups take 32, 64
+ *              or 128 x 256 output tiles from per-XCD device counters, so one
+ *              run leaves no launch gaps between products and no idle CUs
+ *              until its last round. Results are those of zq_gemm, bit for
+ *              bit. Other plans with 32 < m: every problem INT4, k a multiple of 512,
  *              aligned as below; the rows run in chunks of 32 (never a last
  *              chunk of one row), each a plan of its own, so the weights
  *              stream once per chunk. For 2 <= m <= 32, when
@@ -298,7 +301,7 @@ zq_status zq_gemm(const zq_weight* W, const void* X, zq_dtype x_dtype, int64_t m
  * zq_plan_run  enqueues the plan on `stream`: one launch with one workgroup
  *              per CU (cooperative when the plan has more than one phase, so
  *              all workgroups are resident; prefill plans: one launch per
- *              bit width and scale kind, two workgroups per CU); allocates nothing; the run leaves
+ *              bit width and scale kind, two to four workgroups per CU); allocates nothing; the run leaves
  *              the counter at zero for the next one. Runs of one plan that
  *              overlap (on different streams) race on its counter.
  * zq_plan_check synchronises the device and reports ZQ_ERR_HIP if a phase

@@ -79,7 +79,10 @@ int main(void) {
   pr[1].x_dtype = ZQ_F16;
   expect(zq_plan_create(pr, 2, 128, &plan), ZQ_ERR_UNSUPPORTED, "prefill plan, two x types");
   pr[0].w = W(8, 128, 64, 512);
-  expect(zq_plan_create(pr, 1, 48, &plan), ZQ_ERR_UNSUPPORTED, "mid-batch INT8");
+  pr[1].w = W(8, 128, 64, 512);
+  pr[1].x_dtype = ZQ_BF16;
+  pr[1].phase = 1;
+  expect(zq_plan_create(pr, 2, 48, &plan), ZQ_ERR_UNSUPPORTED, "mid-batch INT8 in two phases");
   expect(zq_plan_create(NULL, 0, 1, &plan), ZQ_ERR_INVALID_ARG, "empty list");
   if (plan) ++fails;
   expect(zq_plan_destroy(NULL), ZQ_OK, "destroy null");

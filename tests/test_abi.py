@@ -161,10 +161,12 @@ PLAN_CASES = [
     (128, [(dict(group=0), zq.BF16, 0), (dict(group=0), zq.BF16, 1)], zq.ERR_UNSUPPORTED, "one phase"),
     (128, [(dict(group=0), zq.BF16, 0), (dict(group=0), zq.F16, 0)], zq.ERR_UNSUPPORTED, "one activation type"),
     (128, [(dict(group=0, k=200), zq.BF16, 0)], zq.ERR_UNSUPPORTED, "multiple of 64"),
-    # mid-batch plans (32 < m <= 64): INT4 with k a multiple of 512 only
-    (48, [(dict(bits=8), zq.F16, 0)], zq.ERR_UNSUPPORTED, "INT4"),
-    (60, [(dict(bits=4, k=384), zq.BF16, 0)], zq.ERR_UNSUPPORTED, "multiple of 512"),
-    (40, [(dict(bits=2), zq.BF16, 0)], zq.ERR_UNSUPPORTED, "INT4"),
+    # mid-batch plans with several phases (32 < m <= 64): INT4 with k a
+    # multiple of 512 only (one phase would take the prefill tiles)
+    (48, [(dict(bits=8), zq.F16, 0), (dict(bits=8), zq.F16, 1)], zq.ERR_UNSUPPORTED, "INT4"),
+    (60, [(dict(bits=4, k=384), zq.BF16, 0), (dict(bits=4, k=384), zq.BF16, 1)], zq.ERR_UNSUPPORTED,
+     "multiple of 512"),
+    (40, [(dict(bits=2), zq.BF16, 0), (dict(bits=2), zq.BF16, 1)], zq.ERR_UNSUPPORTED, "INT4"),
 ]
 
 

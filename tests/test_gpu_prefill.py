@@ -218,7 +218,11 @@ def test_prefill_plan_validation():
     with pytest.raises(zq.ZqError) as e:  # activations not 16-byte aligned
         zq.Plan([(W8, X192, Y, 0)])
     assert e.value.status == zq.ERR_UNSUPPORTED
-    X48 = torch.zeros((48, 256), dtype=torch.bfloat16, device=DEV)
-    with pytest.raises(zq.ZqError) as e:  # 32 < m <= 64
-        zq.Plan([(W, X48, torch.empty((48, 64), device=DEV), 0)])
-    assert e.value.status == zq.ERR_UNSUPPORTED
+    # 16 < m <= 64 in one phase: the prefill tiles too (64 rows high here)
+    X48 = torch.randn((48, 256), device=DEV).to(torch.bfloat16)
+    Y48 = torch.full((48, 64), float("nan"), device=DEV)
+    plan = zq.Plan([(W, X48, Y48, 0)])
+    plan.run()
+    torch.cuda.synchronize()
+    plan.check()
+    assert torch.equal(Y48, zq.gemm(W, X48))

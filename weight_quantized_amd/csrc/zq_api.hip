@@ -347,12 +347,16 @@ zq_status zq_gemm(const zq_weight* W, const void* X, zq_dtype x_dtype, int64_t m
   // asymmetric weights: the vector-ALU stream kernel (m = 1), the MFMA
   // batched-decode kernel (INT4) or the general kernel
   const bool asym = W->zeros != nullptr;
-  const bool use_mstream = m >= zq::MSTREAM_MIN_M &&
-                           zq::mstream_supported(W->packed, W->scales, W->zeros, W->bits, W->group, m, W->k, X, ldx);
-  // mid-batch m (up to 64, past which the prefill kernel is faster, or any m
-  // > 32 the prefill kernel does not take): 32-row chunks on the
-  // batched-decode kernel
-  const bool use_chunks = m > 32 && (m <= 64 || !zq::gemm_prefill_supported(a)) &&
+  // the batched-decode kernel streams the weights fastest up to 32 rows;
+  // past that, and for the formats it does not take, symmetric codes go to
+  // the prefill tiles (32, 64 or 128 rows high)
+  const bool mstream_ok = m >= zq::MSTREAM_MIN_M && m <= 32 &&
+                          zq::mstream_supported(W->packed, W->scales, W->zeros, W->bits, W->group, m, W->k, X, ldx);
+  const bool use_prefill = !mstream_ok && !asym && aligned16 && zq::gemm_prefill_supported(a);
+  const bool use_mstream = !use_prefill && mstream_ok;
+  // other m > 32 (asymmetric codes): 32-row chunks on the batched-decode
+  // kernel
+  const bool use_chunks = !use_prefill && m > 32 &&
                           zq::mstream_supported(W->packed, W->scales, W->zeros, W->bits, W->group, 32, W->k, X, ldx);
   if (use_chunks) {
     const int ysz = y_dtype == ZQ_F32 ? 4 : 2;
@@ -398,7 +402,7 @@ zq_status zq_gemm(const zq_weight* W, const void* X, zq_dtype x_dtype, int64_t m
     e = use_stream ? zq::launch_stream_single(p, m, s) : zq::launch_mstream_single(p, m, s);
   } else if (!asym && m <= 4 && aligned16 && zq::gemv_valu_lds_bytes(W->bits, m, W->k) <= 64 * 1024)
     e = zq::launch_gemv_valu(a);
-  else if (!asym && aligned16 && zq::gemm_prefill_supported(a))
+  else if (use_prefill)
     e = zq::launch_gemm_prefill(a);
   else if (!asym && aligned16 && zq::gemm_mfma_supported(a))
     e = zq::launch_gemm_mfma(a);
@@ -421,7 +425,7 @@ struct zq_plan_s {
   int variant = 0;  // the kernel variant of the plan's one format, or the mixed-format one
   int grid = 0;     // workgroups of the launch (the ranges table has one entry per segment and workgroup)
   size_t lds = 0;
-  // prefill plans (m > 64): one tile queue per bit width and group size, run
+  // prefill plans (m > 16): one tile queue per bit width and group size, run
   // in turn
   static constexpr int PREFILL_KINDS = 6;
   bool prefill = false;
@@ -456,7 +460,34 @@ void seg_ranges(const zq::StreamPhase& sg, const std::vector<zq::StreamProblem>&
   }
 }
 
-// A prefill plan (m > 64): every product with symmetric codes, one scale per
+// The products a prefill plan takes for 16 < m <= 64 (batched decode): valid
+// weights, symmetric codes, one phase and activation type, the prefill
+// kernel's shapes and alignment. Other lists go to the batched-decode
+// kernel, which also takes several phases.
+bool prefill_plannable(const zq_problem* problems, int count, int64_t m) {
+  for (int i = 0; i < count; ++i) {
+    const zq_problem& q = problems[i];
+    if (check_weight(&q.w) || q.w.zeros || q.phase != problems[0].phase || q.x_dtype != problems[0].x_dtype ||
+        (q.x_dtype != ZQ_F16 && q.x_dtype != ZQ_BF16) || q.ldx < q.w.k || q.ldy < q.w.n || q.w.n == 0 ||
+        q.w.k == 0 || !q.x || !q.y)
+      return false;
+    zq::GemmArgs a{};
+    a.packed = (const uint8_t*)q.w.packed;
+    a.scales = q.w.scales;
+    a.zeros = q.w.zeros;
+    a.bits = q.w.bits;
+    a.group = q.w.group;
+    a.n = q.w.n;
+    a.k = q.w.k;
+    a.x = (const uint16_t*)q.x;
+    a.m = m;
+    a.ldx = q.ldx;
+    if (!zq::gemm_prefill_supported(a)) return false;
+  }
+  return true;
+}
+
+// A prefill plan (m > 16): every product with symmetric codes, one scale per
 // tensor (k a multiple of 64) or per row and 128 k, 16-byte aligned codes and
 // activations, one activation type, one phase.
 zq_status create_prefill_plan(const zq_problem* problems, int count, int64_t m, zq_plan* plan_out) {
@@ -502,7 +533,7 @@ zq_status create_prefill_plan(const zq_problem* problems, int count, int64_t m, 
     p.k = q.w.k;
     p.ldx = q.ldx;
     p.ldy = q.ldy;
-    p.mtiles = (m + zq::PREFILL_TILE_M - 1) / zq::PREFILL_TILE_M;
+    p.mtiles = (m + zq::prefill_tile_m(m) - 1) / zq::prefill_tile_m(m);
     p.bits = q.w.bits;
     p.group = q.w.group;
     p.yt = q.y_dtype == ZQ_F32 ? zq::YF32 : q.y_dtype == ZQ_F16 ? zq::YF16 : zq::YBF16;
@@ -604,12 +635,27 @@ zq_status zq_plan_create(const zq_problem* problems, int count, int64_t m, zq_pl
   *plan_out = nullptr;
   if (count < 1 || !problems) return fail(ZQ_ERR_INVALID_ARG, "empty problem list");
   if (m < 1) return fail(ZQ_ERR_UNSUPPORTED, "plans take m >= 1 (m=%lld)", (long long)m);
-  if (m > 32) {
-    // symmetric codes and m > 64: the prefill tile queues
-    bool prefill = m > 64;
+  if (m > 64) {
+    // symmetric codes: the prefill tile queues
+    bool prefill = true;
     for (int i = 0; i < count && prefill; ++i) prefill = !problems[i].w.zeros;
     if (prefill) return create_prefill_plan(problems, count, m, plan_out);
     return create_chunked_plan(problems, count, m, plan_out);
+  }
+  if (m > 32) {
+    if (prefill_plannable(problems, count, m)) return create_prefill_plan(problems, count, m, plan_out);
+    return create_chunked_plan(problems, count, m, plan_out);
+  }
+  // 16 < m <= 32: the batched-decode kernel when every product suits it,
+  // else the prefill tiles when they take the list
+  if (m > 16) {
+    bool ms = true;
+    for (int i = 0; i < count && ms; ++i) {
+      const zq_problem& q = problems[i];
+      ms = !check_weight(&q.w) &&
+           zq::mstream_supported(q.w.packed, q.w.scales, q.w.zeros, q.w.bits, q.w.group, m, q.w.k, q.x, q.ldx);
+    }
+    if (!ms && prefill_plannable(problems, count, m)) return create_prefill_plan(problems, count, m, plan_out);
   }
   // the MFMA kernel when every product suits it; for m <= 4 the vector-ALU
   // kernel takes the other formats
@@ -804,7 +850,7 @@ zq_status zq_plan_run(zq_plan plan, void* stream) {
     hipError_t e = hipSuccess;
     for (int g = 0; g < plan->ngroup && e == hipSuccess; ++g)
       e = zq::launch_prefill_plan(plan->pprobs + plan->gfirst[g], plan->gcount[g], plan->gtotal[g], plan->xt,
-                                  plan->gbits[g], plan->ggroup[g], plan->sync + zq::PREFILL_SYNC_WORDS * g,
+                                  plan->gbits[g], plan->ggroup[g], plan->m, plan->sync + zq::PREFILL_SYNC_WORDS * g,
                                   (hipStream_t)stream);
     return e == hipSuccess ? ok() : hip_fail(e, "plan launch");
   }

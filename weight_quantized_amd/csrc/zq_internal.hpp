@@ -89,13 +89,15 @@ hipError_t launch_mstream_plan(const StreamPhase* dev_segs, int nseg, const Stre
 // vector-ALU kernel for m <= 4 with x staged in LDS
 size_t gemv_valu_lds_bytes(int bits, int64_t m, int64_t k);
 hipError_t launch_gemv_valu(const GemmArgs& a);
-// prefill MFMA kernel: m > 64, symmetric codes, one scale per tensor (k a
+// prefill MFMA kernel: m > 16, symmetric codes, one scale per tensor (k a
 // multiple of 64) or per row and 128 k
 bool gemm_prefill_supported(const GemmArgs& a);
 hipError_t launch_gemm_prefill(const GemmArgs& a);
-// One product of a prefill plan (device pointers): its 128 x 256 tiles
-// (PREFILL_TILE_M x PREFILL_TILE_N) are plan tiles [tile0, tile0 + mtiles *
-// ntiles), row block fastest.
+// rows of the kernel's output tiles for m activation rows (32, 64 or 128)
+int prefill_tile_m(int64_t m);
+// One product of a prefill plan (device pointers): its prefill_tile_m(m) x
+// PREFILL_TILE_N tiles are plan tiles [tile0, tile0 + mtiles * ntiles), row
+// block fastest.
 struct PrefillProblem {
   const uint8_t* packed;
   const uint16_t* scales;
@@ -105,13 +107,14 @@ struct PrefillProblem {
   int64_t tile0, mtiles;
   int32_t bits, yt, group;
 };
-constexpr int PREFILL_TILE_M = 128, PREFILL_TILE_N = 256;
+constexpr int PREFILL_TILE_N = 256;
 // persistent launch over the `total` tiles of products of one bit width and
-// group size; xt: their activations' type; sync: PREFILL_SYNC_WORDS device
-// words (tile counters, finished workgroups), zero before the first run
+// group size (m activation rows); xt: their activations' type; sync:
+// PREFILL_SYNC_WORDS device words (tile counters, finished workgroups), zero
+// before the first run
 constexpr int PREFILL_SYNC_WORDS = 16;
 hipError_t launch_prefill_plan(const PrefillProblem* dev_probs, int nprob, int64_t total, int xt, int bits,
-                               int group, uint32_t* sync, hipStream_t stream);
+                               int group, int64_t m, uint32_t* sync, hipStream_t stream);
 // MFMA kernels for larger m
 bool gemm_mfma_supported(const GemmArgs& a);
 hipError_t launch_gemm_mfma(const GemmArgs& a);

@@ -3,5 +3,5 @@
 #include "zq_prefill_impl.hpp"
 
 namespace zq {
-const void* prefill_fn_b8(int xt, bool plan, bool gs) { return prefill_fn<8>(xt, plan, gs); }
+const void* prefill_fn_b8(int xt, bool plan, bool gs, int fi) { return prefill_fn<8>(xt, plan, gs, fi); }
 }  // namespace zq

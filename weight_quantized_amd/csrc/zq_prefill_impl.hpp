@@ -48,9 +48,14 @@
 
 namespace zq {
 
-constexpr int PF_BM = 128, PF_BN = 256, PF_BK = 64, PF_GROUP = 128;
-constexpr int PF_STAGE = PF_BM * PF_BK * 2;  // bytes of one activation stage (16 KB)
-constexpr int PF_NS = 3;                     // activation stages
+constexpr int PF_BN = 256, PF_BK = 64, PF_GROUP = 128;
+constexpr int PF_NS = 3;  // activation stages
+// Tile heights: FI row tiles of 32 (FI = 4 for m > 64; 1 and 2 for the
+// batched-decode range 17..64, where the weights stream once and the matrix
+// cores have time to spare).
+__host__ __device__ constexpr int pf_bm(int fi) { return 32 * fi; }
+__host__ __device__ constexpr int pf_stage(int fi) { return pf_bm(fi) * PF_BK * 2; }  // bytes of one activation stage
+__host__ __device__ constexpr int pf_fi(int64_t m) { return m <= 32 ? 1 : m <= 64 ? 2 : 4; }
 
 template <int XT>
 __device__ __forceinline__ f16v pf_mfma(u4 a, u4 b, f16v c) {
@@ -118,8 +123,16 @@ __device__ __forceinline__ void pf_interleave() {
 // bytes
 __host__ __device__ constexpr int pf_cstage(int bits) { return bits == 8 ? 16384 : 8192; }
 __host__ __device__ constexpr int pf_cr(int bits) { return bits == 2 ? 3 : 2; }
-__host__ __device__ constexpr int pf_lds(int bits) { return PF_NS * PF_STAGE + pf_cr(bits) * pf_cstage(bits); }
-static_assert(pf_lds(2) <= 81920 && pf_lds(4) <= 81920 && pf_lds(8) <= 81920, "two workgroups per CU");
+__host__ __device__ constexpr int pf_lds(int bits, int fi) {
+  return PF_NS * pf_stage(fi) + pf_cr(bits) * pf_cstage(bits);
+}
+// workgroups per CU: 2 (4 with one row tile; 3 for INT8, whose code stages
+// are twice as large)
+__host__ __device__ constexpr int pf_wpc(int bits, int fi) { return fi != 1 ? 2 : bits == 8 ? 3 : 4; }
+static_assert(pf_wpc(2, 4) * pf_lds(2, 4) <= 163840 && pf_wpc(4, 4) * pf_lds(4, 4) <= 163840 &&
+                  pf_wpc(8, 4) * pf_lds(8, 4) <= 163840 && pf_wpc(4, 1) * pf_lds(4, 1) <= 163840 &&
+                  pf_wpc(2, 1) * pf_lds(2, 1) <= 163840 && pf_wpc(8, 1) * pf_lds(8, 1) <= 163840,
+              "the workgroups of a CU share its 160 KB of LDS");
 
 __device__ __forceinline__ float pf_sx(uint32_t w, int b) { return (float)(int)(int8_t)(w >> (8 * b)); }
 __device__ __forceinline__ uint32_t pf_bf(float lo, float hi) {
@@ -325,7 +338,7 @@ struct PfDec<XF16, BITS> {
 // middle barrier), makes the decode keys for group g + 1 and the ratio of
 // old to new units, which the first step of group g + 1 applies to the
 // accumulators before its MFMAs.
-template <int XT, int BITS, int W, bool GS>
+template <int XT, int BITS, int W, bool GS, int FI>
 __device__ __forceinline__ void pf_tile_w(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales,
                                         int64_t n, int64_t k, const uint16_t* __restrict__ x, int64_t m,
                                         int64_t ldx, void* __restrict__ y, int64_t ldy, int yt, int64_t m0,
@@ -337,11 +350,12 @@ __device__ __forceinline__ void pf_tile_w(const uint8_t* __restrict__ packed, co
   // the same cost); group scales: the exact decode
   constexpr bool MAGIC = !GS && !(XT == XBF16 && BITS == 8);
   using MG = PfMagic<XT, BITS>;
-  constexpr int FI = 4, FJ = 2, NS = PF_NS, CR = pf_cr(BITS), CST = pf_cstage(BITS);
+  constexpr int FJ = 2, NS = PF_NS, CR = pf_cr(BITS), CST = pf_cstage(BITS);
+  constexpr int BM = pf_bm(FI), STAGE = pf_stage(FI);
   constexpr int CB = 8 * BITS;  // code bytes of one row per 64-k step
   constexpr int NCL = BITS == 8 ? 2 : 1;
   constexpr int CDMA = BITS == 2 ? 1 : FJ * NCL;  // code loads issued per step
-  constexpr int XDMA = PF_BM / 32;                // activation loads per wave and step
+  constexpr int XDMA = FI;                        // activation loads per wave and step
   // vector memory instructions issued before the middle barrier of a step:
   // the codes two steps ahead and, in the first step of a group, the two
   // scale loads of the next group
@@ -353,19 +367,21 @@ __device__ __forceinline__ void pf_tile_w(const uint8_t* __restrict__ packed, co
   const int KT = (int)(k / PF_BK), G = (int)(k / PF_GROUP);
   const int64_t rowbytes = k * BITS / 8;
 
-  // ---- activations: wave w moves tile rows 32w..32w+31 of each step into
-  // LDS with 4 direct loads of 8 rows x 128 bytes (swizzled as in the
-  // per-tensor tile). Rows past m re-read row m - 1.
-  const int64_t mrows = m - m0 < PF_BM ? m - m0 : PF_BM;
+  // ---- activations: wave w moves tile rows 8FI w .. 8FI w + 8FI - 1 of
+  // each step into LDS with FI direct loads of 8 rows x 128 bytes; lane l of
+  // load c lands at slot l of its 1 KB (row 8FI w + 8c + l/8, position l%8),
+  // so it reads piece (l%8) ^ sw(row) of that row. Rows past m re-read row
+  // m - 1.
+  const int64_t mrows = m - m0 < BM ? m - m0 : BM;
   const __amdgpu_buffer_rsrc_t xr = pf_rsrc(x + m0 * ldx, (uint32_t)(mrows * ldx * 2));
   uint32_t aoff[XDMA];
 #pragma unroll
   for (int c = 0; c < XDMA; ++c) {
-    const int r = 32 * w + 8 * c + (lane >> 3);
+    const int r = 8 * FI * w + 8 * c + (lane >> 3);
     aoff[c] = (uint32_t)((r < mrows ? r : mrows - 1) * ldx * 2 + (((lane & 7) ^ pf_sw(r)) << 4));
   }
   auto dma_x = [&](int ks, int kt) __attribute__((always_inline)) {
-    uint8_t* dst = smem + (kt % NS) * PF_STAGE + 32 * w * 128;
+    uint8_t* dst = smem + (kt % NS) * STAGE + 8 * FI * w * 128;
 #pragma unroll
     for (int c = 0; c < XDMA; ++c)
       __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (__attribute__((address_space(3))) void*)(dst + c * 1024), 16,
@@ -380,7 +396,7 @@ __device__ __forceinline__ void pf_tile_w(const uint8_t* __restrict__ packed, co
     const int r = 64 * w + 32 * j + l32;
     boff[j] = (uint32_t)((r < nrows ? r : nrows - 1) * rowbytes + (BITS == 2 ? 16 : CB / 2) * g);
   }
-  uint8_t* cwave = smem + NS * PF_STAGE + w * (CST / 4);
+  uint8_t* cwave = smem + NS * STAGE + w * (CST / 4);
   auto dma_codes = [&](int ks, int kt) __attribute__((always_inline)) {
     uint8_t* dst = cwave + (kt % CR) * CST;
 #pragma unroll
@@ -459,17 +475,20 @@ __device__ __forceinline__ void pf_tile_w(const uint8_t* __restrict__ packed, co
     }
   };
   // ---- row sums for the magic decode's offsets: in k-step kk the wave sums
-  // the fragment of row tile (kk + W) & 3 it has in registers for its MFMAs
-  // (every row tile and k-step once over the four waves); bs[r]: rows
-  // 32r + l32, k-half g. The four waves' partials are added at the end.
+  // the fragment of row tile (kk + W) & 3, if there is one, that it has in
+  // registers for its MFMAs (every row tile and k-step once over the four
+  // waves); bs[r]: rows 32r + l32, k-half g. The four waves' partials are
+  // added at the end.
   float bs[FI];
 #pragma unroll
   for (int i = 0; i < FI; ++i) bs[i] = 0.f;
   auto bias_sum = [&](const u4 (&a)[FI], int kk) __attribute__((always_inline)) {
     if constexpr (MAGIC) {
       const int r = (kk + W) & 3;
+      if (r < FI) {
 #pragma unroll
-      for (int d = 0; d < 4; ++d) bs[r] = dot2<XT>(a[r][d], MG::BW, bs[r]);
+        for (int d = 0; d < 4; ++d) bs[r] = dot2<XT>(a[r][d], MG::BW, bs[r]);
+      }
     }
   };
   auto rescale = [&]() __attribute__((always_inline)) {
@@ -480,6 +499,7 @@ __device__ __forceinline__ void pf_tile_w(const uint8_t* __restrict__ packed, co
   };
   // decode of one k-step (both fragments) and its row sums
   constexpr int DEC_VALU = MAGIC ? 22 : XT == XF16 ? 26 : BITS == 2 ? 38 : 30;
+  static_assert(FI == 1 || FI == 2 || FI == 4, "row tiles");
 
   u4 a0[FI], a1[FI], b0[FJ], b1[FJ];
   u4 cb[FJ][2], ncb[FJ][2];
@@ -515,8 +535,8 @@ __device__ __forceinline__ void pf_tile_w(const uint8_t* __restrict__ packed, co
 
   // one k-step of 64; ODD: the second step of its group
   auto step = [&]<int ODD>(int kt) __attribute__((always_inline)) {
-    const uint8_t* cur = smem + (kt % NS) * PF_STAGE;
-    const uint8_t* nxt = smem + ((kt + 1) % NS) * PF_STAGE;
+    const uint8_t* cur = smem + (kt % NS) * STAGE;
+    const uint8_t* nxt = smem + ((kt + 1) % NS) * STAGE;
     const int ks = kt + 2 < KT ? kt + 2 : KT - 1;  // past the end: reload the last step
     if constexpr (BITS == 2) {
       const int pt = (kt >> 1) + 2, npair = (KT + 1) >> 1;
@@ -586,18 +606,18 @@ __device__ __forceinline__ void pf_tile_w(const uint8_t* __restrict__ packed, co
   // partials of the two k-halves added, then those of the four waves, in
   // LDS: [wave][row], then the total of row t by thread t)
   pf_barrier<0>();
-  const float* sb = reinterpret_cast<const float*>(smem + 4 * PF_BM * 4);
+  const float* sb = reinterpret_cast<const float*>(smem + 4 * BM * 4);
   if constexpr (MAGIC) {
     float* sbw = reinterpret_cast<float*>(smem);
 #pragma unroll
     for (int i = 0; i < FI; ++i) {
       const float v = bs[i] + __shfl_xor(bs[i], 32, 64);
-      if (g == 0) sbw[w * PF_BM + 32 * i + l32] = v;
+      if (g == 0) sbw[w * BM + 32 * i + l32] = v;
     }
     __syncthreads();
-    if (tid < PF_BM)
-      reinterpret_cast<float*>(smem + 4 * PF_BM * 4)[tid] =
-          u[0] * (sbw[tid] + sbw[PF_BM + tid] + sbw[2 * PF_BM + tid] + sbw[3 * PF_BM + tid]);
+    if (tid < BM)
+      reinterpret_cast<float*>(smem + 4 * BM * 4)[tid] =
+          u[0] * (sbw[tid] + sbw[BM + tid] + sbw[2 * BM + tid] + sbw[3 * BM + tid]);
     __syncthreads();
   }
   auto epi = [&]<int YT, bool EDGE>() __attribute__((always_inline)) {
@@ -625,7 +645,7 @@ __device__ __forceinline__ void pf_tile_w(const uint8_t* __restrict__ packed, co
       }
     }
   };
-  const bool edge = m0 + PF_BM > m || n0 + PF_BN > n;
+  const bool edge = m0 + BM > m || n0 + PF_BN > n;
   if (yt == YF32) {
     if (edge) epi.template operator()<YF32, true>();
     else epi.template operator()<YF32, false>();
@@ -639,16 +659,16 @@ __device__ __forceinline__ void pf_tile_w(const uint8_t* __restrict__ packed, co
   __syncthreads();  // every wave is done with the LDS: the next tile may reuse it
 }
 
-template <int XT, int BITS, bool GS>
+template <int XT, int BITS, bool GS, int FI>
 __device__ __forceinline__ void pf_tile(const uint8_t* __restrict__ packed, const uint16_t* __restrict__ scales,
                                         int64_t n, int64_t k, const uint16_t* __restrict__ x, int64_t m,
                                         int64_t ldx, void* __restrict__ y, int64_t ldy, int yt, int64_t m0,
                                         int64_t n0, uint8_t* smem) {
   switch (__builtin_amdgcn_readfirstlane(threadIdx.x >> 6)) {
-    case 0: pf_tile_w<XT, BITS, 0, GS>(packed, scales, n, k, x, m, ldx, y, ldy, yt, m0, n0, smem); break;
-    case 1: pf_tile_w<XT, BITS, 1, GS>(packed, scales, n, k, x, m, ldx, y, ldy, yt, m0, n0, smem); break;
-    case 2: pf_tile_w<XT, BITS, 2, GS>(packed, scales, n, k, x, m, ldx, y, ldy, yt, m0, n0, smem); break;
-    default: pf_tile_w<XT, BITS, 3, GS>(packed, scales, n, k, x, m, ldx, y, ldy, yt, m0, n0, smem); break;
+    case 0: pf_tile_w<XT, BITS, 0, GS, FI>(packed, scales, n, k, x, m, ldx, y, ldy, yt, m0, n0, smem); break;
+    case 1: pf_tile_w<XT, BITS, 1, GS, FI>(packed, scales, n, k, x, m, ldx, y, ldy, yt, m0, n0, smem); break;
+    case 2: pf_tile_w<XT, BITS, 2, GS, FI>(packed, scales, n, k, x, m, ldx, y, ldy, yt, m0, n0, smem); break;
+    default: pf_tile_w<XT, BITS, 3, GS, FI>(packed, scales, n, k, x, m, ldx, y, ldy, yt, m0, n0, smem); break;
   }
 }
 
@@ -656,18 +676,19 @@ __device__ __forceinline__ void pf_tile(const uint8_t* __restrict__ packed, cons
 // hardware dispatches workgroups x-fastest and deals them out to the 8 XCDs
 // in turn, so consecutive row blocks of one column block keep their
 // activation rows within one XCD's L2 when there are 8k row blocks.
-template <int XT, int BITS, bool GS>
-__global__ __launch_bounds__(256, 2) void prefill_kernel(const uint8_t* __restrict__ packed,
-                                                         const uint16_t* __restrict__ scales, int64_t n, int64_t k,
-                                                         const uint16_t* __restrict__ x, int64_t m, int64_t ldx,
-                                                         void* __restrict__ y, int64_t ldy, int yt) {
+template <int XT, int BITS, bool GS, int FI>
+__global__ __launch_bounds__(256, pf_wpc(BITS, FI)) void prefill_kernel(const uint8_t* __restrict__ packed,
+                                                                  const uint16_t* __restrict__ scales, int64_t n,
+                                                                  int64_t k, const uint16_t* __restrict__ x, int64_t m,
+                                                                  int64_t ldx, void* __restrict__ y, int64_t ldy,
+                                                                  int yt) {
   extern __shared__ __align__(16) uint8_t smem[];
-  pf_tile<XT, BITS, GS>(packed, scales, n, k, x, m, ldx, y, ldy, yt, (int64_t)blockIdx.x * PF_BM,
-                        (int64_t)blockIdx.y * PF_BN, smem);
+  pf_tile<XT, BITS, GS, FI>(packed, scales, n, k, x, m, ldx, y, ldy, yt, (int64_t)blockIdx.x * pf_bm(FI),
+                            (int64_t)blockIdx.y * PF_BN, smem);
 }
 
 // Prefill plan: the tiles of many products of one bit width and scale kind
-// in one persistent launch (two workgroups per CU). Plan order lists
+// in one persistent launch (pf_wpc workgroups per CU). Plan order lists
 // products by decreasing k, each product's tiles with the row block fastest
 // (a product's tile count is a multiple of 8 when its row blocks are). Tile
 // t belongs to queue t % 8, one queue per XCD: with 16 row blocks (m = 2048)
@@ -679,8 +700,8 @@ __global__ __launch_bounds__(256, 2) void prefill_kernel(const uint8_t* __restri
 // zero for the next run.
 constexpr int PP_QUEUES = 8;
 
-template <int XT, int BITS, bool GS>
-__global__ __launch_bounds__(256, 2) void prefill_plan_kernel(const PrefillProblem* __restrict__ probs, int nprob,
+template <int XT, int BITS, bool GS, int FI>
+__global__ __launch_bounds__(256, pf_wpc(BITS, FI)) void prefill_plan_kernel(const PrefillProblem* __restrict__ probs, int nprob,
                                                               int64_t total, uint32_t* __restrict__ sync) {
   extern __shared__ __align__(16) uint8_t smem[];
   // the tile, its product and its row and column blocks pass through the
@@ -730,8 +751,8 @@ __global__ __launch_bounds__(256, 2) void prefill_plan_kernel(const PrefillProbl
     __syncthreads();  // read before the tile's loads and thread 0's next tile
     if (t >= total) break;
     const PrefillProblem& pr = probs[pi];
-    pf_tile<XT, BITS, GS>(pr.packed, pr.scales, pr.n, pr.k, pr.x, pr.m, pr.ldx, pr.y, pr.ldy, pr.yt,
-                          (int64_t)mb * PF_BM, (int64_t)nb * PF_BN, smem);
+    pf_tile<XT, BITS, GS, FI>(pr.packed, pr.scales, pr.n, pr.k, pr.x, pr.m, pr.ldx, pr.y, pr.ldy, pr.yt,
+                              (int64_t)mb * pf_bm(FI), (int64_t)nb * PF_BN, smem);
   }
   if (threadIdx.x == 0 &&
       __hip_atomic_fetch_add(sync + PP_QUEUES, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) == gridDim.x - 1) {
@@ -740,20 +761,25 @@ __global__ __launch_bounds__(256, 2) void prefill_plan_kernel(const PrefillProbl
 }
 
 // kernels of one bit width (instantiated in zq_prefill_b<BITS>.hip): plan ?
-// prefill_plan_kernel : prefill_kernel, for activations of type xt and one
-// scale per 128 k (gs) or per tensor
+// prefill_plan_kernel : prefill_kernel, for activations of type xt, one scale
+// per 128 k (gs) or per tensor, and fi row tiles
 template <int BITS>
-const void* prefill_fn(int xt, bool plan, bool gs) {
-  auto pick = [&]<int XT>() -> const void* {
-    if (gs) return plan ? reinterpret_cast<const void*>(&prefill_plan_kernel<XT, BITS, true>)
-                        : reinterpret_cast<const void*>(&prefill_kernel<XT, BITS, true>);
-    return plan ? reinterpret_cast<const void*>(&prefill_plan_kernel<XT, BITS, false>)
-                : reinterpret_cast<const void*>(&prefill_kernel<XT, BITS, false>);
+const void* prefill_fn(int xt, bool plan, bool gs, int fi) {
+  auto pick = [&]<int XT, bool G, int FI>() -> const void* {
+    return plan ? reinterpret_cast<const void*>(&prefill_plan_kernel<XT, BITS, G, FI>)
+                : reinterpret_cast<const void*>(&prefill_kernel<XT, BITS, G, FI>);
   };
-  return xt == XF16 ? pick.template operator()<XF16>() : pick.template operator()<XBF16>();
+  auto by_fi = [&]<int XT, bool G>() -> const void* {
+    return fi == 1 ? pick.template operator()<XT, G, 1>()
+                   : fi == 2 ? pick.template operator()<XT, G, 2>() : pick.template operator()<XT, G, 4>();
+  };
+  auto by_gs = [&]<int XT>() -> const void* {
+    return gs ? by_fi.template operator()<XT, true>() : by_fi.template operator()<XT, false>();
+  };
+  return xt == XF16 ? by_gs.template operator()<XF16>() : by_gs.template operator()<XBF16>();
 }
-const void* prefill_fn_b2(int xt, bool plan, bool gs);
-const void* prefill_fn_b4(int xt, bool plan, bool gs);
-const void* prefill_fn_b8(int xt, bool plan, bool gs);
+const void* prefill_fn_b2(int xt, bool plan, bool gs, int fi);
+const void* prefill_fn_b4(int xt, bool plan, bool gs, int fi);
+const void* prefill_fn_b8(int xt, bool plan, bool gs, int fi);
 
 }  // namespace zq
