@@ -229,7 +229,11 @@ zq_status zq_gemv(const zq_weight* W, const void* x, zq_dtype x_dtype, void* y,
  *   Y       device, m rows of n elements, row stride ldy >= n, dtype ZQ_F32,
  *           ZQ_F16 or ZQ_BF16.
  * Kernels by shape (all give results within the same tolerance of the exact
- * sums; integer-valued inputs give exact sums on every path). Asymmetric
+ * sums; integer-valued inputs give exact sums on every path but one: the
+ * group-scaled prefill tiles (m > 32) move their fp32 accumulators from one
+ * group's scale to the next by a rounded ratio, exact only when the scales
+ * of a row differ by powers of two, so there a one-hot row is a few ulp off
+ * w_deq). Asymmetric
  * weights take the first three paths below, else the general kernel:
  *   m = 1, k a multiple of 128 (m <= 4 where the MFMA kernel below does
  *     not apply): a vector-ALU kernel that streams the codes once with

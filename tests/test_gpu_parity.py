@@ -264,6 +264,30 @@ def test_one_hot_rows_recover_dequantized_columns(m):
     x = np.zeros((m, k), dtype=np.float16)
     x[np.arange(m), cols] = 1
     y = run_gemm(W, x, "f16")
+    ref = O.dequant(q, 128, s)[:, cols].T
+    if m <= 32:
+        assert np.array_equal(y, ref)
+    else:
+        # the group-scaled prefill tile changes its accumulators' units at
+        # each group boundary by a rounded ratio (one here, k / 128 - 1 in
+        # general): a few ulp off the exact value
+        assert np.all(np.abs(y - ref) <= 4e-7 * (k // 128) * np.abs(ref))
+
+
+@pytest.mark.parametrize("xdt", ["f16", "bf16"])
+def test_prefill_group_one_hot_power_of_two_scales_exact(xdt):
+    # with power-of-two group scales every change of units is exact, so the
+    # group-scaled prefill tile recovers dequantized columns bit for bit
+    m, n, k = 128, 96, 1024
+    g = synth.rng(11)
+    q = synth.codes_uniform(g, n, k, 4)
+    s = g.choice(np.array([0x3400, 0x3800, 0x3C00, 0x4000], dtype=np.uint16), size=n * k // 128)
+    q, s, p, W = make_weight(4, 128, n, k, 0, codes=q, scales=s)
+    cols = np.arange(m) * 13 % k
+    x = np.zeros((m, k), dtype=np.float16)
+    x[np.arange(m), cols] = 1
+    xx = x if xdt == "f16" else synth.f32_to_bf16_bits(x.astype(np.float32))
+    y = run_gemm(W, xx, xdt)
     assert np.array_equal(y, O.dequant(q, 128, s)[:, cols].T)
 
 
