@@ -431,9 +431,11 @@ def extras(a, base: Stack, torch, zq, synth) -> dict:
     t = measure(st.plan_step, 2000, 50, torch, settle_s=0.05)
     kern = t["ms_mean_of_steps"]
     f = decode_figures(st, t, kern)
+    # back-to-back calls: the interval between launches, not the kernel's own
+    # duration (about 7 us by trace), is the figure
     out["config1_gemv512"] = {"us_per_call": round(t["ms"] * 1e3, 3),
                               "us_per_call_median": round(t["ms_median"] * 1e3, 3),
-                              "kernel_us": round(kern * 1e3, 3), "value": f["value"], "unit": "GB/s",
+                              "value": f["value"], "unit": "GB/s",
                               "roofline": {"bound": "latency", "note": "131,074 weight bytes fit in L2; "
                                            "µs per call is the figure", "hbm_frac": f["hbm_frac"]},
                               "workload": "512x512 INT4, per-tensor fp16(0.02), M=1, fp16 x, plan launches "
