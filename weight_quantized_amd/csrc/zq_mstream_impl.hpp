@@ -50,9 +50,9 @@ namespace zq {
 // 256-row blocks and use the same transpose scratch. At M = 2..16 the 16
 // waves streamed 11-23 % faster than 8.
 template <int MT>
-__host__ __device__ constexpr int ms_threads() { return MT == 1 ? 1024 : 512; }
+__host__ __device__ constexpr int ms_threads() { return 1024; }
 template <int MT>
-__host__ __device__ constexpr int ms_tw() { return MT == 1 ? 1 : 2; }  // 16-row tiles per wave per block
+__host__ __device__ constexpr int ms_tw() { return 1; }  // 16-row tiles per wave per block
 constexpr int MS_KC = 512;       // k per chunk (4 groups of 128)
 constexpr int MS_BLOCK = 256;  // rows per block: waves x tiles per wave x 16
 static_assert(ms_threads<1>() / 64 * ms_tw<1>() * 16 == MS_BLOCK && ms_threads<2>() / 64 * ms_tw<2>() * 16 == MS_BLOCK,
@@ -91,6 +91,9 @@ struct MDec {
   static constexpr float BE = (XT == XF16 ? 1024.f : 128.f) + FLIP;  // pairs of even k
   static constexpr float BO = (XT == XF16 ? 64.f : 128.f) + FLIP;    // pairs of odd k
   static constexpr uint32_t S0 = ASYM ? 0u : 0x00080008u, S1 = ASYM ? 0u : 0x00800080u;
+  // (BE, BO) and (1, 1) as 16-bit pairs of the activation type
+  static constexpr uint32_t BW = XT == XF16 ? (ASYM ? 0x54006400u : 0x54806408u) : (ASYM ? 0x43004300u : 0x43084308u);
+  static constexpr uint32_t ONE = XT == XF16 ? 0x3C003C00u : 0x3F803F80u;
   static __device__ __forceinline__ u4 decode(uint32_t v) {
     u4 r;
     if constexpr (XT == XF16) {
@@ -234,9 +237,8 @@ __device__ __forceinline__ bool run_msegment(const StreamPhase& seg, const Strea
       const int p = i * NT + tid;
       const int mm = p >> 6, k8 = p & 63;
       const int gs = k8 >> 4, gg = (k8 >> 2) & 3, d = k8 & 3, mt = mm >> 4, m16 = mm & 15;
-      const bool live = mm < m;
-      const uint32_t a0 = live ? xr[i][0] : 0u, a1 = live ? xr[i][1] : 0u;
-      const uint32_t a2 = live ? xr[i][2] : 0u, a3 = live ? xr[i][3] : 0u;
+      // rows past m hold row 0 again: their outputs are never stored
+      const uint32_t a0 = xr[i][0], a1 = xr[i][1], a2 = xr[i][2], a3 = xr[i][3];
       // natural order x0..x7 -> decoder pair order (0,4),(1,5),(2,6),(3,7)
       u4 piece;
       piece[0] = (a0 & 0xFFFFu) | (a2 << 16);
@@ -244,12 +246,11 @@ __device__ __forceinline__ bool run_msegment(const StreamPhase& seg, const Strea
       piece[2] = (a1 & 0xFFFFu) | (a3 << 16);
       piece[3] = (a1 >> 16) | (a3 & 0xFFFF0000u);
       *reinterpret_cast<u4*>(buf + ((((gs * MT + mt) * 4 + d) * 4 + gg) * 16 + m16) * 16) = piece;
-      const float se = x_bits_to_float<XT>((uint16_t)(a0 & 0xFFFFu)) + x_bits_to_float<XT>((uint16_t)(a1 & 0xFFFFu)) +
-                       x_bits_to_float<XT>((uint16_t)(a2 & 0xFFFFu)) + x_bits_to_float<XT>((uint16_t)(a3 & 0xFFFFu));
-      const float so = x_bits_to_float<XT>((uint16_t)(a0 >> 16)) + x_bits_to_float<XT>((uint16_t)(a1 >> 16)) +
-                       x_bits_to_float<XT>((uint16_t)(a2 >> 16)) + x_bits_to_float<XT>((uint16_t)(a3 >> 16));
-      float corr = D::BE * se + D::BO * so;
-      float sum = se + so;
+      // BE * (x at even k) + BO * (x at odd k), as dot products of pairs
+      float corr = dot2<XT>(a0, D::BW, dot2<XT>(a1, D::BW, dot2<XT>(a2, D::BW, dot2<XT>(a3, D::BW, 0.f))));
+      float sum = 0.f;
+      if constexpr (ASYM)
+        sum = dot2<XT>(a0, D::ONE, dot2<XT>(a1, D::ONE, dot2<XT>(a2, D::ONE, dot2<XT>(a3, D::ONE, 0.f))));
       // the 16 pieces of one (row, group) are 16 aligned consecutive threads
 #pragma unroll
       for (int o = 1; o < 16; o <<= 1) {
@@ -310,6 +311,52 @@ __device__ __forceinline__ bool run_msegment(const StreamPhase& seg, const Strea
       for (int s4 = 0; s4 < 4; ++s4)
         slot[SB + 4 * t + s4] = __builtin_nontemporal_load(to_global(w_ptr(pf, t, s4)));
     __builtin_amdgcn_wave_barrier();
+    if constexpr (TW == 1) {
+      // one weight tile per wave: the activation fragments are read one
+      // activation tile at a time, so two tiles fit 128 VGPRs
+#pragma unroll
+      for (int gs = 0; gs < 4; ++gs) {
+        __builtin_amdgcn_sched_barrier(0);
+        const u4 wq = *reinterpret_cast<const u4*>(wscr + (n16 >> 2) * MS_TLOAD + (n16 & 3) * MS_TROW + (4 * gs + g) * 16);
+        if (it.b0 + wv * 16 < it.b1) {  // wave-uniform: the tile has rows
+          u4 bw[4];
+#pragma unroll
+          for (int d = 0; d < 4; ++d) bw[d] = D::decode(wq[d]);
+          float s = 1.f, z = 0.f;
+          if constexpr (GROUPED) {
+            const uint32_t sw = sc[CB2][gs >> 1];
+            s = f16_bits_to_float((uint16_t)((gs & 1) ? (sw >> 16) : (sw & 0xFFFFu)));
+          }
+          if constexpr (ASYM) {
+            const uint32_t zw = zc[CB2][gs >> 1];
+            z = f16_bits_to_float((uint16_t)((gs & 1) ? (zw >> 16) : (zw & 0xFFFFu)));
+          }
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            u4 a[4];
+#pragma unroll
+            for (int d = 0; d < 4; ++d)
+              a[d] = *reinterpret_cast<const u4*>(buf + ((((gs * MT + mt) * 4 + d) * 4 + g) * 16 + n16) * 16);
+            f4 dd = *reinterpret_cast<const f4*>(buf + MT * 16384 + ((gs * MT + mt) * 16 + 4 * g) * 4);
+            f4 xsum;
+            if constexpr (ASYM)
+              xsum = *reinterpret_cast<const f4*>(buf + MT * 16640 + ((gs * MT + mt) * 16 + 4 * g) * 4);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) dd = ms_mfma<XT>(a[d], bw[d], dd);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              if constexpr (GROUPED) acc[0][mt][j] = __builtin_fmaf(s, dd[j], acc[0][mt][j]);
+              else acc[0][mt][j] += dd[j];
+              if constexpr (ASYM) acc[0][mt][j] = __builtin_fmaf(z, xsum[j], acc[0][mt][j]);
+            }
+          }
+        }
+        if constexpr (GROUPED)
+          if (gs == 3) sc[CB2] = *to_global(s_ptr(pf, 0));
+        if constexpr (ASYM)
+          if (gs == 3) zc[CB2] = *to_global(z_ptr(pf, 0));
+      }
+    } else {
 #pragma unroll
     for (int gs = 0; gs < 4; ++gs) {
       u4 a[MT][4];
@@ -359,6 +406,7 @@ __device__ __forceinline__ bool run_msegment(const StreamPhase& seg, const Strea
         if constexpr (ASYM)
           if (gs == 3) zc[CB2 + t] = *to_global(z_ptr(pf, t));
       }
+    }
     }
     if (it.c == NC - 1) epilogue(it);
     store_x(xbuf + (H ^ 1) * XB);
