@@ -44,22 +44,18 @@
 
 namespace zq {
 
-// One 16-row activation tile (M <= 16): 16 waves with one 16-row weight
-// tile each per block; two (M = 17..32): 8 waves with two each, since the
-// second tile's accumulators and fragments do not fit 128 VGPRs. Both walk
-// 256-row blocks and use the same transpose scratch. At M = 2..16 the 16
-// waves streamed 11-23 % faster than 8.
+// 16 waves per workgroup; wave w takes 16-row weight tile w of each
+// 256-row block, against one 16-row activation tile (M <= 16) or two
+// (M = 17..32). With two, the activation fragments are read from LDS one
+// tile at a time, so both tiles' accumulators fit 128 VGPRs. 16 waves
+// streamed 11-23 % faster than 8 at M = 2..16 and 8-11 % faster at
+// M = 17..32 (where 8 waves had held two weight tiles each).
 template <int MT>
 __host__ __device__ constexpr int ms_threads() { return 1024; }
-template <int MT>
-__host__ __device__ constexpr int ms_tw() { return 1; }  // 16-row tiles per wave per block
-constexpr int MS_KC = 512;       // k per chunk (4 groups of 128)
-constexpr int MS_BLOCK = 256;  // rows per block: waves x tiles per wave x 16
-static_assert(ms_threads<1>() / 64 * ms_tw<1>() * 16 == MS_BLOCK && ms_threads<2>() / 64 * ms_tw<2>() * 16 == MS_BLOCK,
-              "both tile counts walk the same blocks");
-// items whose weights are in flight ahead of the one computed: 1 (64 KB per
-// CU) streamed 0.4-1 % faster than 2 at M = 2..64, with ~40 fewer VGPRs
-constexpr int MS_AHEAD = 1;
+constexpr int MS_KC = 512;     // k per chunk (4 groups of 128)
+constexpr int MS_BLOCK = 256;  // rows per block: 16 waves x 16 rows
+static_assert(ms_threads<1>() / 64 * 16 == MS_BLOCK && ms_threads<2>() / 64 * 16 == MS_BLOCK,
+              "one weight tile per wave and block");
 
 // LDS bytes of one activation chunk buffer: A fragments [gs][mt][d][g][m][8]
 // (16 bytes each), the negated offset sums [gs][mt][m] (fp32) and, for
@@ -137,8 +133,6 @@ __device__ __forceinline__ bool run_msegment(const StreamPhase& seg, const Strea
   constexpr bool coherent = COH;
   using D = MDec<XT, ASYM>;
   constexpr int NT = ms_threads<MT>();
-  constexpr int NWV = NT / 64;  // waves
-  constexpr int TW = ms_tw<MT>();
   constexpr int XB = mstream_xbuf_bytes(MT);
   constexpr int PPT = MT * 16 * 64 / NT;  // activation pieces (8 values) per thread per chunk
 
@@ -159,7 +153,7 @@ __device__ __forceinline__ bool run_msegment(const StreamPhase& seg, const Strea
 
   ProdRec* rec = reinterpret_cast<ProdRec*>(smem);
   uint8_t* xbuf = smem + (size_t)nrec * sizeof(ProdRec);
-  uint8_t* wscr = xbuf + 2 * XB + wv * TW * MS_TTILE;  // this wave's transpose scratch
+  uint8_t* wscr = xbuf + 2 * XB + wv * MS_TTILE;  // this wave's transpose scratch
   for (int i = tid; i < nrec; i += NT) {
     const StreamProblem& p = probs ? probs[seg.first + wr.x + i] : single;
     rec[i] = make_rec(p, rowbytes, GS, GROUPED);
@@ -171,11 +165,14 @@ __device__ __forceinline__ bool run_msegment(const StreamPhase& seg, const Strea
   struct Item {
     int32_t pi, b0, b1, c;
   };
+  // record fields come from LDS: readfirstlane tells the compiler they are
+  // the same in every lane, so the item state stays in scalar registers
+  auto pend_of = [&](int i) __attribute__((always_inline)) { return __builtin_amdgcn_readfirstlane(rec[i].pend); };
   auto first_item = [&]() __attribute__((always_inline)) {
     Item it;
-    it.pi = rec_of(rec, nrec, r0);
+    it.pi = __builtin_amdgcn_readfirstlane(rec_of(rec, nrec, r0));
     it.b0 = r0;
-    it.b1 = min(min(r0 + MS_BLOCK, r1), rec[it.pi].pend);
+    it.b1 = min(min(r0 + MS_BLOCK, r1), pend_of(it.pi));
     it.c = 0;
     return it;
   };
@@ -184,51 +181,87 @@ __device__ __forceinline__ bool run_msegment(const StreamPhase& seg, const Strea
     if (++it.c < NC) return it;
     it.c = 0;
     it.b0 = it.b1;
-    if (it.b0 >= rec[it.pi].pend) ++it.pi;
-    it.b1 = it.b0 < r1 ? min(min(it.b0 + MS_BLOCK, r1), rec[min(it.pi, nrec - 1)].pend) : it.b0;
+    if (it.b0 >= pend_of(it.pi)) ++it.pi;
+    it.b1 = it.b0 < r1 ? min(min(it.b0 + MS_BLOCK, r1), pend_of(min(it.pi, nrec - 1))) : it.b0;
     return it;
   };
-  // the next item, or the same one past the end (a valid stand-in address)
-  auto next_or_same = [&](const Item& it) __attribute__((always_inline)) {
-    const Item nx = next_item(it);
-    return valid(nx) ? nx : it;
-  };
 
-  // ---- weight stream: 4 register slots per lane, tile and item in flight,
-  // for this wave's TW tiles; slot 4TWh + 4t + s holds rows 4s..4s+3 of tile
-  // t of an item (of parity h when two are in flight; lane l: row 4s + l/16,
-  // bytes 16*(l%16) of the chunk). Slots are refilled with the item MS_AHEAD
-  // ahead as soon as they are moved to LDS.
-  // Loads are unconditional (tiles past a block's end re-read its last row),
-  // so the compiler counts them exactly.
-  u4 slot[4 * TW * MS_AHEAD];
-  u2 sc[TW * MS_AHEAD], zc[TW * MS_AHEAD];
-  auto w_ptr = [&](const Item& it, int t, int s4) __attribute__((always_inline)) {
-    const ProdRec& pr = rec[it.pi];
-    const int32_t row = min(it.b0 + (wv + NWV * t) * 16 + 4 * s4 + (lane >> 4), it.b1 - 1);
-    return reinterpret_cast<const u4*>(pr.wbase + (int64_t)row * rowbytes + (int64_t)it.c * 256) + (lane & 15);
+  // ---- fetch state of the item whose weights, scales and activations are
+  // being loaded. Buffer loads: a descriptor per block (weights, scales, zero
+  // points: the block's rows only) or per product (activations: m rows), a
+  // scalar offset per item and a per-lane offset that is fixed for the
+  // segment. Lane l of a weight load takes row 4 s + l/16 of the wave's tile
+  // (slot s), bytes 16 (l % 16) of the chunk. Rows past the block's end and
+  // activation rows past m lie outside their descriptor and read as zeros
+  // (their outputs are never stored), so every load is unconditional and
+  // the compiler counts them exactly.
+  __amdgpu_buffer_rsrc_t f_w, f_s, f_z, f_x;
+  int32_t f_wo, f_so, f_xo;  // scalar byte offsets of the item
+  int32_t f_ldxb;  // activation row pitch in bytes
+  const uint32_t wvo = (uint32_t)(lane >> 4) * (uint32_t)rowbytes + (uint32_t)(lane & 15) * 16;
+  const uint32_t svo = (uint32_t)n16 * (uint32_t)(GS * 2);
+  const uint32_t xvo = (uint32_t)lane * 16;
+  // Descriptor words must sit in scalar registers: a descriptor held in
+  // vector registers turns every load into a loop over lanes. Record fields
+  // read from LDS are the same in every lane, which readfirstlane states.
+  auto uni = [](const void* p) __attribute__((always_inline)) {
+    const uint64_t v = (uint64_t)(uintptr_t)p;
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (const uint8_t*)(uintptr_t)(((uint64_t)hi << 32) | lo);
   };
-  auto s_ptr = [&](const Item& it, int t) __attribute__((always_inline)) {
-    const ProdRec& pr = rec[it.pi];
-    const int32_t row = min(it.b0 + (wv + NWV * t) * 16 + n16, it.b1 - 1);
-    return reinterpret_cast<const u2*>(pr.sbase + (int64_t)row * GS + 4 * it.c);
+  auto rsrc = [&](const void* base, uint32_t bytes) __attribute__((always_inline)) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(uni(base)), (short)0,
+                                             (int)__builtin_amdgcn_readfirstlane(bytes), 0x00020000);
   };
-  auto z_ptr = [&](const Item& it, int t) __attribute__((always_inline)) {
+  auto fetch_block = [&](const Item& it) __attribute__((always_inline)) {
     const ProdRec& pr = rec[it.pi];
-    const int32_t row = min(it.b0 + (wv + NWV * t) * 16 + n16, it.b1 - 1);
-    return reinterpret_cast<const u2*>(pr.zbase + (int64_t)row * GS + 4 * it.c);
+    const uint32_t rows = (uint32_t)(it.b1 - it.b0);
+    f_w = rsrc(uni(pr.wbase) + (int64_t)it.b0 * rowbytes, rows * (uint32_t)rowbytes);
+    if constexpr (GROUPED) f_s = rsrc(uni(pr.sbase) + (int64_t)it.b0 * GS * 2, rows * (uint32_t)(GS * 2));
+    if constexpr (ASYM) f_z = rsrc(uni(pr.zbase) + (int64_t)it.b0 * GS * 2, rows * (uint32_t)(GS * 2));
+    f_ldxb = __builtin_amdgcn_readfirstlane((int32_t)pr.ldx * 2);
+    f_x = rsrc(uni(pr.x), (uint32_t)m * (uint32_t)f_ldxb);
+    f_wo = wv * 16 * (int32_t)rowbytes + it.c * 256;
+    f_so = wv * 16 * GS * 2 + it.c * 8;
+    f_xo = it.c * MS_KC * 2;
+  };
+  // move the fetch state from item `from` to the next item `to`
+  auto fetch_advance = [&](const Item& from, const Item& to) __attribute__((always_inline)) {
+    if (to.b0 != from.b0) {  // uniform: a new block
+      fetch_block(to);
+    } else {
+      f_wo += 256;
+      f_so += 8;
+      f_xo += MS_KC * 2;
+    }
+  };
+  constexpr int AUX_NT = 2, AUX_COH = 16;  // cache policy: nontemporal; agent-coherent (sc1)
+
+  // ---- weight stream: 4 register slots per lane hold the next item's
+  // weights (64 KB per workgroup); they are refilled as soon as the current
+  // item's are moved to the wave's LDS scratch. One item ahead streamed
+  // 0.4-1 % faster than two at M = 2..64, with ~40 fewer VGPRs.
+  u4 slot[4];
+  u2 sc = u2{0u, 0u}, zc = u2{0u, 0u};
+  auto fetch_weights = [&]() __attribute__((always_inline)) {
+#pragma unroll
+    for (int s4 = 0; s4 < 4; ++s4)
+      slot[s4] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(
+                                            f_w, (int)wvo, f_wo + s4 * 4 * (int32_t)rowbytes, AUX_NT));
+  };
+  auto fetch_scales = [&]() __attribute__((always_inline)) {
+    if constexpr (GROUPED) sc = __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(f_s, (int)svo, f_so, 0));
+    if constexpr (ASYM) zc = __builtin_bit_cast(u2, __builtin_amdgcn_raw_buffer_load_b64(f_z, (int)svo, f_so, 0));
   };
 
   // ---- activations of one item: MT*16 rows x 512 k, PPT pieces per thread
   u4 xr[PPT];
-  auto load_x = [&](const Item& it) __attribute__((always_inline)) {
-    const ProdRec& pr = rec[it.pi];
+  auto load_x = [&]() __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < PPT; ++i) {
-      const int p = i * NT + tid;
-      const int mm = p >> 6, k8 = p & 63;
-      // rows past m re-read row 0 and are zeroed when stored
-      xr[i] = load_x16(pr.x + (int64_t)(mm < m ? mm : 0) * pr.ldx + (int64_t)it.c * MS_KC + 8 * k8, coherent);
+      const int mm = i * (NT / 64) + wv;  // activation row of piece i (uniform)
+      xr[i] = __builtin_bit_cast(u4, __builtin_amdgcn_raw_buffer_load_b128(f_x, (int)xvo, mm * f_ldxb + f_xo,
+                                                                           coherent ? AUX_COH : 0));
     }
   };
   auto store_x = [&](uint8_t* buf) __attribute__((always_inline)) {
@@ -237,7 +270,6 @@ __device__ __forceinline__ bool run_msegment(const StreamPhase& seg, const Strea
       const int p = i * NT + tid;
       const int mm = p >> 6, k8 = p & 63;
       const int gs = k8 >> 4, gg = (k8 >> 2) & 3, d = k8 & 3, mt = mm >> 4, m16 = mm & 15;
-      // rows past m hold row 0 again: their outputs are never stored
       const uint32_t a0 = xr[i][0], a1 = xr[i][1], a2 = xr[i][2], a3 = xr[i][3];
       // natural order x0..x7 -> decoder pair order (0,4),(1,5),(2,6),(3,7)
       u4 piece;
@@ -264,175 +296,91 @@ __device__ __forceinline__ bool run_msegment(const StreamPhase& seg, const Strea
     }
   };
 
-  f4 acc[TW][MT];
+  f4 acc[MT];
 #pragma unroll
-  for (int t = 0; t < TW; ++t)
-#pragma unroll
-    for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int mt = 0; mt < MT; ++mt) acc[mt] = f4{0.f, 0.f, 0.f, 0.f};
 
   auto epilogue = [&](const Item& it) __attribute__((always_inline)) {
     const ProdRec& pr = rec[it.pi];
+    const int32_t row = it.b0 + wv * 16 + n16;
 #pragma unroll
-    for (int t = 0; t < TW; ++t) {
-      const int32_t row = it.b0 + (wv + NWV * t) * 16 + n16;
+    for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int mm = mt * 16 + 4 * g + j;
-          if (mm < m && row < it.b1)
-            store_y_coherent(pr.y, (int64_t)mm * pr.ldy + (row - pr.roff), acc[t][mt][j] * pr.tscale, pr.yt,
-                             coherent);
-          acc[t][mt][j] = 0.f;
-        }
+      for (int j = 0; j < 4; ++j) {
+        const int mm = mt * 16 + 4 * g + j;
+        if (mm < m && row < it.b1)
+          store_y_coherent(pr.y, (int64_t)mm * pr.ldy + (row - pr.roff), acc[mt][j] * pr.tscale, pr.yt, coherent);
+        acc[mt][j] = 0.f;
       }
     }
   };
 
-  // One item of parity H: x for it is in LDS buffer H; the slots hold its
-  // weights. Loads the next item's activations and refills the slots with
-  // the item MS_AHEAD ahead (`nx`, or `pf2` two ahead), then stages the
-  // activations and waits for the workgroup.
-  auto process = [&]<int H>(const Item& it, const Item& nx, const Item& pf2) __attribute__((always_inline)) {
+  // One item of parity H: its activations are in LDS buffer H, its weights
+  // in the slots and its scales in sc/zc; the fetch state points at the next
+  // item (or at this one again when it is the last). Loads the next item's
+  // activations, moves this item's weights to the scratch and refills the
+  // slots, computes, then stages the next activations and waits for the
+  // workgroup.
+  auto process = [&]<int H>(const Item& it) __attribute__((always_inline)) {
     const uint8_t* buf = xbuf + H * XB;
-    constexpr int SB = MS_AHEAD == 2 ? 4 * TW * H : 0, CB2 = MS_AHEAD == 2 ? TW * H : 0;
-    const Item& pf = MS_AHEAD == 2 ? pf2 : nx;
-    load_x(nx);
-    // this item's weights -> the wave's scratch; refill the slots at once
+    load_x();
 #pragma unroll
-    for (int t = 0; t < TW; ++t)
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4)
-        *reinterpret_cast<u4*>(wscr + t * MS_TTILE + s4 * MS_TLOAD + (lane >> 4) * MS_TROW + (lane & 15) * 16) =
-            slot[SB + 4 * t + s4];
-#pragma unroll
-    for (int t = 0; t < TW; ++t)
-#pragma unroll
-      for (int s4 = 0; s4 < 4; ++s4)
-        slot[SB + 4 * t + s4] = __builtin_nontemporal_load(to_global(w_ptr(pf, t, s4)));
+    for (int s4 = 0; s4 < 4; ++s4)
+      *reinterpret_cast<u4*>(wscr + s4 * MS_TLOAD + (lane >> 4) * MS_TROW + (lane & 15) * 16) = slot[s4];
+    fetch_weights();
     __builtin_amdgcn_wave_barrier();
-    if constexpr (TW == 1) {
-      // one weight tile per wave: the activation fragments are read one
-      // activation tile at a time, so two tiles fit 128 VGPRs
-#pragma unroll
-      for (int gs = 0; gs < 4; ++gs) {
-        __builtin_amdgcn_sched_barrier(0);
-        const u4 wq = *reinterpret_cast<const u4*>(wscr + (n16 >> 2) * MS_TLOAD + (n16 & 3) * MS_TROW + (4 * gs + g) * 16);
-        if (it.b0 + wv * 16 < it.b1) {  // wave-uniform: the tile has rows
-          u4 bw[4];
-#pragma unroll
-          for (int d = 0; d < 4; ++d) bw[d] = D::decode(wq[d]);
-          float s = 1.f, z = 0.f;
-          if constexpr (GROUPED) {
-            const uint32_t sw = sc[CB2][gs >> 1];
-            s = f16_bits_to_float((uint16_t)((gs & 1) ? (sw >> 16) : (sw & 0xFFFFu)));
-          }
-          if constexpr (ASYM) {
-            const uint32_t zw = zc[CB2][gs >> 1];
-            z = f16_bits_to_float((uint16_t)((gs & 1) ? (zw >> 16) : (zw & 0xFFFFu)));
-          }
-#pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            u4 a[4];
-#pragma unroll
-            for (int d = 0; d < 4; ++d)
-              a[d] = *reinterpret_cast<const u4*>(buf + ((((gs * MT + mt) * 4 + d) * 4 + g) * 16 + n16) * 16);
-            f4 dd = *reinterpret_cast<const f4*>(buf + MT * 16384 + ((gs * MT + mt) * 16 + 4 * g) * 4);
-            f4 xsum;
-            if constexpr (ASYM)
-              xsum = *reinterpret_cast<const f4*>(buf + MT * 16640 + ((gs * MT + mt) * 16 + 4 * g) * 4);
-#pragma unroll
-            for (int d = 0; d < 4; ++d) dd = ms_mfma<XT>(a[d], bw[d], dd);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              if constexpr (GROUPED) acc[0][mt][j] = __builtin_fmaf(s, dd[j], acc[0][mt][j]);
-              else acc[0][mt][j] += dd[j];
-              if constexpr (ASYM) acc[0][mt][j] = __builtin_fmaf(z, xsum[j], acc[0][mt][j]);
-            }
-          }
-        }
-        if constexpr (GROUPED)
-          if (gs == 3) sc[CB2] = *to_global(s_ptr(pf, 0));
-        if constexpr (ASYM)
-          if (gs == 3) zc[CB2] = *to_global(z_ptr(pf, 0));
-      }
-    } else {
+    const u2 scur = sc, zcur = zc;
+    fetch_scales();
+    const bool rows = it.b0 + wv * 16 < it.b1;  // wave-uniform: the tile has rows
 #pragma unroll
     for (int gs = 0; gs < 4; ++gs) {
-      u4 a[MT][4];
-      f4 cneg[MT], xsum[MT];
+      __builtin_amdgcn_sched_barrier(0);
+      // row n16 of the tile, bytes 64 gs + 16 g: load n16/4, row n16%4, piece 4 gs + g
+      const u4 wq = *reinterpret_cast<const u4*>(wscr + (n16 >> 2) * MS_TLOAD + (n16 & 3) * MS_TROW + (4 * gs + g) * 16);
+      if (rows) {
+        u4 bw[4];
 #pragma unroll
-      for (int mt = 0; mt < MT; ++mt) {
+        for (int d = 0; d < 4; ++d) bw[d] = D::decode(wq[d]);
+        float s = 1.f, z = 0.f;
+        if constexpr (GROUPED) {
+          const uint32_t sw = scur[gs >> 1];
+          s = f16_bits_to_float((uint16_t)((gs & 1) ? (sw >> 16) : (sw & 0xFFFFu)));
+        }
+        if constexpr (ASYM) {
+          const uint32_t zw = zcur[gs >> 1];
+          z = f16_bits_to_float((uint16_t)((gs & 1) ? (zw >> 16) : (zw & 0xFFFFu)));
+        }
 #pragma unroll
-        for (int d = 0; d < 4; ++d)
-          a[mt][d] = *reinterpret_cast<const u4*>(buf + ((((gs * MT + mt) * 4 + d) * 4 + g) * 16 + n16) * 16);
-        cneg[mt] = *reinterpret_cast<const f4*>(buf + MT * 16384 + ((gs * MT + mt) * 16 + 4 * g) * 4);
-        if constexpr (ASYM)
-          xsum[mt] = *reinterpret_cast<const f4*>(buf + MT * 16640 + ((gs * MT + mt) * 16 + 4 * g) * 4);
-      }
+        for (int mt = 0; mt < MT; ++mt) {
+          u4 a[4];
 #pragma unroll
-      for (int t = 0; t < TW; ++t) {
-        // row n16 of the tile, bytes 64 gs + 16 g: load n16/4, row n16%4, piece 4 gs + g
-        const u4 wq = *reinterpret_cast<const u4*>(wscr + t * MS_TTILE + (n16 >> 2) * MS_TLOAD +
-                                                   (n16 & 3) * MS_TROW + (4 * gs + g) * 16);
-        if (it.b0 + (wv + NWV * t) * 16 < it.b1) {  // wave-uniform: the tile has rows
-          u4 bw[4];
+          for (int d = 0; d < 4; ++d)
+            a[d] = *reinterpret_cast<const u4*>(buf + ((((gs * MT + mt) * 4 + d) * 4 + g) * 16 + n16) * 16);
+          f4 dd = *reinterpret_cast<const f4*>(buf + MT * 16384 + ((gs * MT + mt) * 16 + 4 * g) * 4);
+          f4 xsum;
+          if constexpr (ASYM) xsum = *reinterpret_cast<const f4*>(buf + MT * 16640 + ((gs * MT + mt) * 16 + 4 * g) * 4);
 #pragma unroll
-          for (int d = 0; d < 4; ++d) bw[d] = D::decode(wq[d]);
-          float s = 1.f, z = 0.f;
-          if constexpr (GROUPED) {
-            const uint32_t sw = sc[CB2 + t][gs >> 1];
-            s = f16_bits_to_float((uint16_t)((gs & 1) ? (sw >> 16) : (sw & 0xFFFFu)));
-          }
-          if constexpr (ASYM) {
-            const uint32_t zw = zc[CB2 + t][gs >> 1];
-            z = f16_bits_to_float((uint16_t)((gs & 1) ? (zw >> 16) : (zw & 0xFFFFu)));
-          }
+          for (int d = 0; d < 4; ++d) dd = ms_mfma<XT>(a[d], bw[d], dd);
 #pragma unroll
-          for (int mt = 0; mt < MT; ++mt) {
-            f4 dd = cneg[mt];
-#pragma unroll
-            for (int d = 0; d < 4; ++d) dd = ms_mfma<XT>(a[mt][d], bw[d], dd);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              if constexpr (GROUPED) acc[t][mt][j] = __builtin_fmaf(s, dd[j], acc[t][mt][j]);
-              else acc[t][mt][j] += dd[j];
-              if constexpr (ASYM) acc[t][mt][j] = __builtin_fmaf(z, xsum[mt][j], acc[t][mt][j]);
-            }
+          for (int j = 0; j < 4; ++j) {
+            if constexpr (GROUPED) acc[mt][j] = __builtin_fmaf(s, dd[j], acc[mt][j]);
+            else acc[mt][j] += dd[j];
+            if constexpr (ASYM) acc[mt][j] = __builtin_fmaf(z, xsum[j], acc[mt][j]);
           }
         }
-        if constexpr (GROUPED)
-          if (gs == 3) sc[CB2 + t] = *to_global(s_ptr(pf, t));
-        if constexpr (ASYM)
-          if (gs == 3) zc[CB2 + t] = *to_global(z_ptr(pf, t));
       }
-    }
     }
     if (it.c == NC - 1) epilogue(it);
     store_x(xbuf + (H ^ 1) * XB);
     __syncthreads();  // also orders this wave's scratch reads before the next item's writes
   };
 
-  // ---- prologue: the first MS_AHEAD items' weights (they do not depend on
-  // earlier phases), then the phase wait, then the first activations
+  // ---- prologue: the first item's weights and scales (they do not depend
+  // on earlier phases), then the phase wait, then the first activations
   Item cur = first_item();
-  Item nx = next_or_same(cur);
-#pragma unroll
-  for (int t = 0; t < TW; ++t) {
-#pragma unroll
-    for (int s4 = 0; s4 < 4; ++s4) {
-      slot[4 * t + s4] = __builtin_nontemporal_load(to_global(w_ptr(cur, t, s4)));
-      if constexpr (MS_AHEAD == 2) slot[(MS_AHEAD - 1) * 4 * TW + 4 * t + s4] = __builtin_nontemporal_load(to_global(w_ptr(nx, t, s4)));
-    }
-    if constexpr (GROUPED) {
-      sc[t] = *to_global(s_ptr(cur, t));
-      if constexpr (MS_AHEAD == 2) sc[(MS_AHEAD - 1) * TW + t] = *to_global(s_ptr(nx, t));
-    }
-    if constexpr (ASYM) {
-      zc[t] = *to_global(z_ptr(cur, t));
-      if constexpr (MS_AHEAD == 2) zc[(MS_AHEAD - 1) * TW + t] = *to_global(z_ptr(nx, t));
-    }
-  }
+  fetch_block(cur);
+  fetch_weights();
+  fetch_scales();
   if (sync) {
     if (tid == 0) {
       uint32_t polls = 0;
@@ -446,23 +394,26 @@ __device__ __forceinline__ bool run_msegment(const StreamPhase& seg, const Strea
     }
     __syncthreads();
   }
-  load_x(cur);
+  load_x();
   store_x(xbuf);
   __syncthreads();
 
-  // ---- main loop: two items per trip so slot and buffer indices are static
-  Item pf = next_or_same(nx);
+  // ---- main loop: two items per trip so the buffer index is static; the
+  // fetch state moves to the next item before each one is processed (past
+  // the last item it stays, and the loads repeat valid addresses)
   while (true) {
-    nx = next_item(cur);
-    process.template operator()<0>(cur, valid(nx) ? nx : cur, pf);
-    if (!valid(nx)) break;
+    Item nx = next_item(cur);
+    bool more = valid(nx);
+    if (more) fetch_advance(cur, nx);
+    process.template operator()<0>(cur);
+    if (!more) break;
     cur = nx;
-    pf = next_or_same(pf);
     nx = next_item(cur);
-    process.template operator()<1>(cur, valid(nx) ? nx : cur, pf);
-    if (!valid(nx)) break;
+    more = valid(nx);
+    if (more) fetch_advance(cur, nx);
+    process.template operator()<1>(cur);
+    if (!more) break;
     cur = nx;
-    pf = next_or_same(pf);
   }
   __syncthreads();  // LDS is reused by the next segment
   return true;
