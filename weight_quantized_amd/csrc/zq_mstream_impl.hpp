@@ -58,7 +58,10 @@ static_assert(ms_threads<1>() / 64 * 16 == MS_BLOCK && ms_threads<2>() / 64 * 16
               "one weight tile per wave and block");
 
 // LDS bytes of one activation chunk buffer: A fragments [gs][mt][d][g][m][8]
-// (16 bytes each), the negated offset sums [gs][mt][m] (fp32) and, for
+// (16 bytes each; row m of fragment (d, g) at slot m ^ (4 d + g), so that a
+// wave staging one activation row writes 16 different bank groups with 16
+// consecutive lanes, while the 16 lanes of an MFMA read still cover one
+// 256-byte run), the negated offset sums [gs][mt][m] (fp32) and, for
 // asymmetric weights, the plain sums [gs][mt][m] (fp32).
 __host__ __device__ constexpr int mstream_xbuf_bytes(int mt) { return mt * (4 * 4 * 4 * 16 * 16 + 2 * 4 * 16 * 4); }
 // Weight transpose scratch of one wave: per tile, 4 loads x 4 rows x 16
@@ -277,7 +280,7 @@ __device__ __forceinline__ bool run_msegment(const StreamPhase& seg, const Strea
       piece[1] = (a0 >> 16) | (a2 & 0xFFFF0000u);
       piece[2] = (a1 & 0xFFFFu) | (a3 << 16);
       piece[3] = (a1 >> 16) | (a3 & 0xFFFF0000u);
-      *reinterpret_cast<u4*>(buf + ((((gs * MT + mt) * 4 + d) * 4 + gg) * 16 + m16) * 16) = piece;
+      *reinterpret_cast<u4*>(buf + ((((gs * MT + mt) * 4 + d) * 4 + gg) * 16 + (m16 ^ (4 * d + gg))) * 16) = piece;
       // BE * (x at even k) + BO * (x at odd k), as dot products of pairs
       float corr = dot2<XT>(a0, D::BW, dot2<XT>(a1, D::BW, dot2<XT>(a2, D::BW, dot2<XT>(a3, D::BW, 0.f))));
       float sum = 0.f;
@@ -355,7 +358,7 @@ __device__ __forceinline__ bool run_msegment(const StreamPhase& seg, const Strea
           u4 a[4];
 #pragma unroll
           for (int d = 0; d < 4; ++d)
-            a[d] = *reinterpret_cast<const u4*>(buf + ((((gs * MT + mt) * 4 + d) * 4 + g) * 16 + n16) * 16);
+            a[d] = *reinterpret_cast<const u4*>(buf + ((((gs * MT + mt) * 4 + d) * 4 + g) * 16 + (n16 ^ (4 * d + g))) * 16);
           f4 dd = *reinterpret_cast<const f4*>(buf + MT * 16384 + ((gs * MT + mt) * 16 + 4 * g) * 4);
           f4 xsum;
           if constexpr (ASYM) xsum = *reinterpret_cast<const f4*>(buf + MT * 16640 + ((gs * MT + mt) * 16 + 4 * g) * 4);
