@@ -286,12 +286,9 @@ __device__ __forceinline__ bool run_msegment(const StreamPhase& seg, const Strea
       float sum = 0.f;
       if constexpr (ASYM)
         sum = dot2<XT>(a0, D::ONE, dot2<XT>(a1, D::ONE, dot2<XT>(a2, D::ONE, dot2<XT>(a3, D::ONE, 0.f))));
-      // the 16 pieces of one (row, group) are 16 aligned consecutive threads
-#pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        corr += __shfl_xor(corr, o, 64);
-        if constexpr (ASYM) sum += __shfl_xor(sum, o, 64);
-      }
+      // the 16 pieces of one (row, group) are the 16 lanes of a DPP row
+      corr = row16_sum(corr);
+      if constexpr (ASYM) sum = row16_sum(sum);
       if ((k8 & 15) == 0) {
         *reinterpret_cast<float*>(buf + MT * 16384 + ((gs * MT + mt) * 16 + m16) * 4) = -corr;
         if constexpr (ASYM) *reinterpret_cast<float*>(buf + MT * 16640 + ((gs * MT + mt) * 16 + m16) * 4) = sum;
