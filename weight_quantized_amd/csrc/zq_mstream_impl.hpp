@@ -52,10 +52,17 @@ namespace zq {
 // M = 17..32 (where 8 waves had held two weight tiles each).
 template <int MT>
 __host__ __device__ constexpr int ms_threads() { return 1024; }
-constexpr int MS_KC = 512;     // k per chunk (4 groups of 128)
-constexpr int MS_BLOCK = 256;  // rows per block: 16 waves x 16 rows
-static_assert(ms_threads<1>() / 64 * 16 == MS_BLOCK && ms_threads<2>() / 64 * 16 == MS_BLOCK,
-              "one weight tile per wave and block");
+// Weight tiles a wave takes in turn against the same staged activations:
+// with two activation tiles (M = 17..32) a block is 512 rows, walked as two
+// 256-row halves per chunk, so the activations are staged (and re-read from
+// L2) once per 512 rows instead of once per 256. Zero points need more
+// registers; asymmetric weights keep 256-row blocks.
+template <int MT, bool ASYM>
+__host__ __device__ constexpr int ms_tp() { return MT == 2 && !ASYM ? 2 : 1; }
+constexpr int MS_KC = 512;    // k per chunk (4 groups of 128)
+constexpr int MS_HALF = 256;  // rows of one half of a block: 16 waves x 16 rows
+static_assert(ms_threads<1>() / 64 * 16 == MS_HALF && ms_threads<2>() / 64 * 16 == MS_HALF,
+              "one weight tile per wave and half");
 
 // LDS bytes of one activation chunk buffer: A fragments [gs][mt][d][g][m][8]
 // (16 bytes each; row m of fragment (d, g) at slot m ^ (4 d + g), so that a
@@ -68,7 +75,7 @@ __host__ __device__ constexpr int mstream_xbuf_bytes(int mt) { return mt * (4 * 
 // pieces of 16 bytes, each 16-piece row padded by 16 bytes (272 bytes) so
 // that both the row-wise writes and the tile-column reads are conflict-free.
 constexpr int MS_TROW = 272, MS_TLOAD = 4 * MS_TROW, MS_TTILE = 4 * MS_TLOAD;
-constexpr int MS_WSCR_ALL = (MS_BLOCK / 16) * MS_TTILE;  // all waves' scratch of one workgroup
+constexpr int MS_WSCR_ALL = (MS_HALF / 16) * MS_TTILE;  // all waves' scratch of one workgroup
 
 __host__ __device__ inline size_t mstream_lds_bytes(int mt, int nrec) {
   return (size_t)nrec * PROD_REC_BYTES + 2 * (size_t)mstream_xbuf_bytes(mt) + (size_t)MS_WSCR_ALL;
@@ -138,6 +145,8 @@ __device__ __forceinline__ bool run_msegment(const StreamPhase& seg, const Strea
   constexpr int NT = ms_threads<MT>();
   constexpr int XB = mstream_xbuf_bytes(MT);
   constexpr int PPT = MT * 16 * 64 / NT;  // activation pieces (8 values) per thread per chunk
+  constexpr int TP = ms_tp<MT, ASYM>();
+  constexpr int BLOCK = TP * MS_HALF;  // rows per block
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -163,10 +172,11 @@ __device__ __forceinline__ bool run_msegment(const StreamPhase& seg, const Strea
   }
   __syncthreads();
 
-  // ---- the workgroup's item sequence: blocks of <= 256 rows inside one
-  // product, each in NC chunks. Item state is workgroup-uniform.
+  // ---- the workgroup's item sequence: blocks of <= BLOCK rows inside one
+  // product, each in NC chunks of TP halves (h). Item state is
+  // workgroup-uniform.
   struct Item {
-    int32_t pi, b0, b1, c;
+    int32_t pi, b0, b1, c, h;
   };
   // record fields come from LDS: readfirstlane tells the compiler they are
   // the same in every lane, so the item state stays in scalar registers
@@ -175,17 +185,20 @@ __device__ __forceinline__ bool run_msegment(const StreamPhase& seg, const Strea
     Item it;
     it.pi = __builtin_amdgcn_readfirstlane(rec_of(rec, nrec, r0));
     it.b0 = r0;
-    it.b1 = min(min(r0 + MS_BLOCK, r1), pend_of(it.pi));
+    it.b1 = min(min(r0 + BLOCK, r1), pend_of(it.pi));
     it.c = 0;
+    it.h = 0;
     return it;
   };
   auto valid = [&](const Item& it) __attribute__((always_inline)) { return it.b0 < r1; };
   auto next_item = [&](Item it) __attribute__((always_inline)) {
+    if (++it.h < TP) return it;
+    it.h = 0;
     if (++it.c < NC) return it;
     it.c = 0;
     it.b0 = it.b1;
     if (it.b0 >= pend_of(it.pi)) ++it.pi;
-    it.b1 = it.b0 < r1 ? min(min(it.b0 + MS_BLOCK, r1), pend_of(min(it.pi, nrec - 1))) : it.b0;
+    it.b1 = it.b0 < r1 ? min(min(it.b0 + BLOCK, r1), pend_of(min(it.pi, nrec - 1))) : it.b0;
     return it;
   };
 
@@ -224,17 +237,20 @@ __device__ __forceinline__ bool run_msegment(const StreamPhase& seg, const Strea
     if constexpr (ASYM) f_z = rsrc(uni(pr.zbase) + (int64_t)it.b0 * GS * 2, rows * (uint32_t)(GS * 2));
     f_ldxb = __builtin_amdgcn_readfirstlane((int32_t)pr.ldx * 2);
     f_x = rsrc(uni(pr.x), (uint32_t)m * (uint32_t)f_ldxb);
-    f_wo = wv * 16 * (int32_t)rowbytes + it.c * 256;
-    f_so = wv * 16 * GS * 2 + it.c * 8;
+    f_wo = (it.h * MS_HALF + wv * 16) * (int32_t)rowbytes + it.c * 256;
+    f_so = (it.h * MS_HALF + wv * 16) * GS * 2 + it.c * 8;
     f_xo = it.c * MS_KC * 2;
   };
   // move the fetch state from item `from` to the next item `to`
   auto fetch_advance = [&](const Item& from, const Item& to) __attribute__((always_inline)) {
     if (to.b0 != from.b0) {  // uniform: a new block
       fetch_block(to);
-    } else {
-      f_wo += 256;
-      f_so += 8;
+    } else if (to.c == from.c) {  // the next half of the same chunk
+      f_wo += MS_HALF * (int32_t)rowbytes;
+      f_so += MS_HALF * GS * 2;
+    } else {  // the first half of the next chunk
+      f_wo += 256 - (TP - 1) * MS_HALF * (int32_t)rowbytes;
+      f_so += 8 - (TP - 1) * MS_HALF * GS * 2;
       f_xo += MS_KC * 2;
     }
   };
@@ -296,34 +312,40 @@ __device__ __forceinline__ bool run_msegment(const StreamPhase& seg, const Strea
     }
   };
 
-  f4 acc[MT];
+  f4 acc[TP][MT];
 #pragma unroll
-  for (int mt = 0; mt < MT; ++mt) acc[mt] = f4{0.f, 0.f, 0.f, 0.f};
+  for (int t = 0; t < TP; ++t)
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) acc[t][mt] = f4{0.f, 0.f, 0.f, 0.f};
 
-  auto epilogue = [&](const Item& it) __attribute__((always_inline)) {
+  auto epilogue = [&]<int T>(const Item& it) __attribute__((always_inline)) {
     const ProdRec& pr = rec[it.pi];
-    const int32_t row = it.b0 + wv * 16 + n16;
+    const int32_t row = it.b0 + T * MS_HALF + wv * 16 + n16;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int mm = mt * 16 + 4 * g + j;
         if (mm < m && row < it.b1)
-          store_y_coherent(pr.y, (int64_t)mm * pr.ldy + (row - pr.roff), acc[mt][j] * pr.tscale, pr.yt, coherent);
-        acc[mt][j] = 0.f;
+          store_y_coherent(pr.y, (int64_t)mm * pr.ldy + (row - pr.roff), acc[T][mt][j] * pr.tscale, pr.yt,
+                           coherent);
+        acc[T][mt][j] = 0.f;
       }
     }
   };
 
-  // One item of parity H: its activations are in LDS buffer H, its weights
-  // in the slots and its scales in sc/zc; the fetch state points at the next
-  // item (or at this one again when it is the last). Loads the next item's
-  // activations, moves this item's weights to the scratch and refills the
-  // slots, computes, then stages the next activations and waits for the
-  // workgroup.
-  auto process = [&]<int H>(const Item& it) __attribute__((always_inline)) {
+  // One item (half T of a chunk of parity H): the chunk's activations are in
+  // LDS buffer H, the item's weights in the slots and its scales in sc/zc;
+  // the fetch state points at the next item (or at this one again when it
+  // is the last). Moves this item's weights to the scratch and refills the
+  // slots, computes; in a chunk's last half it also loads the next chunk's
+  // activations, stages them into the other buffer and waits for the
+  // workgroup (the only barrier of the chunk: each wave's scratch is its
+  // own, and the activation buffers alternate by chunk).
+  auto process = [&]<int H, int T>(const Item& it) __attribute__((always_inline)) {
+    constexpr bool last_half = T == TP - 1;
     const uint8_t* buf = xbuf + H * XB;
-    load_x();
+    if constexpr (last_half) load_x();
 #pragma unroll
     for (int s4 = 0; s4 < 4; ++s4)
       *reinterpret_cast<u4*>(wscr + s4 * MS_TLOAD + (lane >> 4) * MS_TROW + (lane & 15) * 16) = slot[s4];
@@ -331,7 +353,7 @@ __device__ __forceinline__ bool run_msegment(const StreamPhase& seg, const Strea
     __builtin_amdgcn_wave_barrier();
     const u2 scur = sc, zcur = zc;
     fetch_scales();
-    const bool rows = it.b0 + wv * 16 < it.b1;  // wave-uniform: the tile has rows
+    const bool rows = it.b0 + T * MS_HALF + wv * 16 < it.b1;  // wave-uniform: the tile has rows
 #pragma unroll
     for (int gs = 0; gs < 4; ++gs) {
       __builtin_amdgcn_sched_barrier(0);
@@ -363,16 +385,18 @@ __device__ __forceinline__ bool run_msegment(const StreamPhase& seg, const Strea
           for (int d = 0; d < 4; ++d) dd = ms_mfma<XT>(a[d], bw[d], dd);
 #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            if constexpr (GROUPED) acc[mt][j] = __builtin_fmaf(s, dd[j], acc[mt][j]);
-            else acc[mt][j] += dd[j];
-            if constexpr (ASYM) acc[mt][j] = __builtin_fmaf(z, xsum[j], acc[mt][j]);
+            if constexpr (GROUPED) acc[T][mt][j] = __builtin_fmaf(s, dd[j], acc[T][mt][j]);
+            else acc[T][mt][j] += dd[j];
+            if constexpr (ASYM) acc[T][mt][j] = __builtin_fmaf(z, xsum[j], acc[T][mt][j]);
           }
         }
       }
     }
-    if (it.c == NC - 1) epilogue(it);
-    store_x(xbuf + (H ^ 1) * XB);
-    __syncthreads();  // also orders this wave's scratch reads before the next item's writes
+    if (it.c == NC - 1) epilogue.template operator()<T>(it);
+    if constexpr (last_half) {
+      store_x(xbuf + (H ^ 1) * XB);
+      __syncthreads();
+    }
   };
 
   // ---- prologue: the first item's weights and scales (they do not depend
@@ -398,22 +422,26 @@ __device__ __forceinline__ bool run_msegment(const StreamPhase& seg, const Strea
   store_x(xbuf);
   __syncthreads();
 
-  // ---- main loop: two items per trip so the buffer index is static; the
-  // fetch state moves to the next item before each one is processed (past
-  // the last item it stays, and the loads repeat valid addresses)
+  // ---- main loop: two chunks (2 TP items) per trip so the buffer and half
+  // indices are static; the fetch state moves to the next item before each
+  // one is processed (past the last item it stays, and the loads repeat
+  // valid addresses). Every block starts at half 0 of chunk 0 and has
+  // NC * TP items, so the item at each position has that position's half.
+  auto step = [&]<int H, int T>() __attribute__((always_inline)) {
+    const Item nx = next_item(cur);
+    const bool more = valid(nx);
+    if (more) fetch_advance(cur, nx);
+    process.template operator()<H, T>(cur);
+    cur = nx;
+    return more;
+  };
   while (true) {
-    Item nx = next_item(cur);
-    bool more = valid(nx);
-    if (more) fetch_advance(cur, nx);
-    process.template operator()<0>(cur);
-    if (!more) break;
-    cur = nx;
-    nx = next_item(cur);
-    more = valid(nx);
-    if (more) fetch_advance(cur, nx);
-    process.template operator()<1>(cur);
-    if (!more) break;
-    cur = nx;
+    if (!step.template operator()<0, 0>()) break;
+    if constexpr (TP == 2)
+      if (!step.template operator()<0, 1>()) break;
+    if (!step.template operator()<1, 0>()) break;
+    if constexpr (TP == 2)
+      if (!step.template operator()<1, 1>()) break;
   }
   __syncthreads();  // LDS is reused by the next segment
   return true;
