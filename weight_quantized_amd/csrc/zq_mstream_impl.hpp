@@ -17,48 +17,49 @@
 //     decoded weight codes the B operand: MFMA output column n is weight row
 //     n of the tile, so each lane multiplies by the group scale of the one
 //     weight row it loaded;
-//   * weights are loaded with one load instruction covering 4 rows x 256
-//     contiguous bytes (16 lanes per row); in the MFMA layout one instruction
-//     would cover 16 rows x 64 bytes, which streams ~25% slower from HBM. The
-//     wave then moves each 16-row tile through a padded LDS scratch so that
-//     lane (row n, slot g) holds the 16 bytes (32 codes) of row n at byte
-//     64*group + 16*g; those codes feed 4 MFMAs, 8 codes each, in the
-//     decoder's pair order; activations are staged in LDS in that same order,
-//     so A and B agree on k;
+//   * weights are loaded with buffer loads, one instruction covering 4 rows
+//     x 256 contiguous bytes (16 lanes per row); in the MFMA layout one
+//     instruction would cover 16 rows x 64 bytes, which streams ~25% slower
+//     from HBM. The wave then moves each 16-row tile through a padded LDS
+//     scratch so that lane (row n, slot g) holds the 16 bytes (32 codes) of
+//     row n at byte 64*group + 16*g; those codes feed 4 MFMAs, 8 codes each,
+//     in the decoder's pair order; activations are staged in LDS in that
+//     same order, so A and B agree on k;
 //   * codes become exact 16-bit values with a constant offset (a nibble
 //     placed in a binary16/bfloat16 fraction); the offset's contribution,
 //     BE * (sum of x at even k) + BO * (sum at odd k) per activation row and
 //     group, is staged with the activations and enters the first MFMA of the
 //     group as its C operand, negated, so the MFMA output is the group's
 //     exact-input dot product;
-//   * a workgroup (16 waves for up to 16 activation rows, 8 for more) owns
-//     a contiguous range of the segment's row space; it walks it in blocks
-//     of up to 256 rows inside one product (wave w takes 16-row tile w, or
-//     tiles w and w + 8 with 8 waves) and each block in chunks
-//     of 512 k: activations of the next chunk are loaded into registers and
-//     the weights of the next chunk are in flight while the current chunk is
-//     computed; the activation buffers in LDS are double buffered;
-//   * outputs of a block are stored when its last chunk is done.
+//   * a workgroup of 16 waves owns a contiguous range of the segment's row
+//     space; it walks it in blocks of up to 512 rows inside one product
+//     (256 for asymmetric weights), each block in chunks of 512 k and each
+//     chunk in 256-row halves; wave w takes 16-row tile w of each half.
+//     The next item's weights are in flight while the current one is
+//     computed; the next chunk's activations are loaded during a chunk's
+//     last half and staged into the other of two LDS buffers;
+//   * outputs of a half are stored when its last chunk is done.
 #pragma once
 #include "zq_stream_impl.hpp"
 
 namespace zq {
 
 // 16 waves per workgroup; wave w takes 16-row weight tile w of each
-// 256-row block, against one 16-row activation tile (M <= 16) or two
+// 256-row half block, against one 16-row activation tile (M <= 16) or two
 // (M = 17..32). With two, the activation fragments are read from LDS one
 // tile at a time, so both tiles' accumulators fit 128 VGPRs. 16 waves
 // streamed 11-23 % faster than 8 at M = 2..16 and 8-11 % faster at
 // M = 17..32 (where 8 waves had held two weight tiles each).
 template <int MT>
 __host__ __device__ constexpr int ms_threads() { return 1024; }
-// Weight tiles a wave takes in turn against the same staged activations:
-// with two activation tiles (M = 17..32) a block is 512 rows, walked as two
-// 256-row halves per chunk, so the activations are staged (and re-read from
-// L2) once per 512 rows instead of once per 256. Zero points need more
-// registers; asymmetric weights keep 256-row blocks.
+// Weight tiles a wave takes in turn against the same staged activations: a
+// block is 512 rows, walked as two 256-row halves per chunk, so the
+// activations are staged (and re-read from L2) once per 512 rows instead of
+// once per 256, with one workgroup barrier per chunk (M = 17..32: 5-6 %
+// faster, M = 8..16: 2-3 %). Zero points need more registers: asymmetric
+// weights keep 256-row blocks.
 template <int MT, bool ASYM>
-__host__ __device__ constexpr int ms_tp() { return MT == 2 && !ASYM ? 2 : 1; }
+__host__ __device__ constexpr int ms_tp() { return ASYM ? 1 : 2; }
 constexpr int MS_KC = 512;    // k per chunk (4 groups of 128)
 constexpr int MS_HALF = 256;  // rows of one half of a block: 16 waves x 16 rows
 static_assert(ms_threads<1>() / 64 * 16 == MS_HALF && ms_threads<2>() / 64 * 16 == MS_HALF,
