@@ -57,14 +57,17 @@ constexpr int st_threads() { return MR == 1 ? 1024 : 512; }
 //    (value 1024 + u), pairs (1,5),(3,7) in bits 7:4 (value 64 + u); one shift
 //    by 8 serves the upper two pairs. u = q + 8. Offsets: even k 1032, odd 72.
 //  fp16 INT8: bytes in the fraction's low 8 bits: value 1024 + u, u = q + 128.
+//  bf16 INT4: every pair's nibbles in the fraction's low 4 bits (value
+//    128 + u, u = q + 8) after shifts by 0, 4, 8 and 12; offset 136 for all k.
 //  everything else: the generic Decoder (one offset for all k).
 // ASYM: unsigned codes (u = code, no sign flip), so every offset is smaller
 // by 2^(BITS-1): fp16 INT4 1024 / 64, generic 2^BITS.
 template <int XT, int BITS, bool ASYM = false>
 struct FastDec {
-  static constexpr float SYM_BE = (XT == XF16 && BITS == 4) ? 1032.f
-                                  : (XT == XF16 && BITS == 8) ? 1152.f
-                                                              : Decoder<XT, BITS>::BIAS;
+  static constexpr float SYM_BE = (XT == XF16 && BITS == 4)    ? 1032.f
+                                  : (XT == XF16 && BITS == 8)  ? 1152.f
+                                  : (XT == XBF16 && BITS == 4) ? 136.f
+                                                               : Decoder<XT, BITS>::BIAS;
   static constexpr float SYM_BO = (XT == XF16 && BITS == 4) ? 72.f : SYM_BE;
   static constexpr float BE = ASYM ? SYM_BE - (float)(1 << (BITS - 1)) : SYM_BE;
   static constexpr float BO = ASYM ? SYM_BO - (float)(1 << (BITS - 1)) : SYM_BO;
@@ -81,6 +84,12 @@ struct FastDec {
       d = dot2<XF16>((v & 0x00F000F0u) ^ (FLIP4H ^ 0x54005400u), xq[1], d);
       d = dot2<XF16>((t & 0x000F000Fu) ^ (FLIP4 ^ 0x64006400u), xq[2], d);
       d = dot2<XF16>((t & 0x00F000F0u) ^ (FLIP4H ^ 0x54005400u), xq[3], d);
+      return d;
+    } else if constexpr (XT == XBF16 && BITS == 4) {
+      d = dot2<XBF16>((v & 0x000F000Fu) ^ (FLIP4 ^ 0x43004300u), xq[0], d);
+      d = dot2<XBF16>(((v >> 4) & 0x000F000Fu) ^ (FLIP4 ^ 0x43004300u), xq[1], d);
+      d = dot2<XBF16>(((v >> 8) & 0x000F000Fu) ^ (FLIP4 ^ 0x43004300u), xq[2], d);
+      d = dot2<XBF16>(((v >> 12) & 0x000F000Fu) ^ (FLIP4 ^ 0x43004300u), xq[3], d);
       return d;
     } else if constexpr (XT == XF16 && BITS == 8) {
       d = dot2<XF16>((v & 0x00FF00FFu) ^ (FLIP8 ^ 0x64006400u), xq[0], d);
