@@ -117,6 +117,47 @@ def test_mstream_plan_matches_oracle_and_single_calls(m):
         check(Y.double().cpu().numpy(), O.gemm(p, 4, s, group, n, k, x, xdt), x, xdt, q, group, s)
 
 
+@pytest.mark.parametrize("m", [8, 17, 32])
+def test_mstream_plan_long_ranges(m):
+    """Workgroup ranges of several hundred rows: 512-row blocks with both
+    256-row halves live, a partial second half, blocks that end at a product
+    boundary, one and two 512-k chunks. Every 5th row and the rows around each
+    workgroup's range and each 256-row half are checked against the oracle."""
+    ncu = torch.cuda.get_device_properties(0).multi_processor_count
+    spec = [(128, 41000, 512, 0), (128, 69000, 512, 1), (0, 150000, 1024, 2)]  # (group, n, k, seed)
+    probs, refs = [], []
+    for group, n, k, sd in spec:
+        q, s, p, W = weight(4, group, n, k, seed=700 + sd)
+        x = synth.normal(synth.rng(800 + sd), (m, k), "bf16")
+        Y = torch.full((m, n), float("nan"), device=DEV)
+        probs.append((W, x_dev(x, "bf16"), Y, 0))
+        refs.append((q, s, p, x, group, n, k))
+    plan = zq.Plan(probs)
+    plan.run()
+    torch.cuda.synchronize()
+    plan.check()
+    # segments: (group 0, k 1024) then (group 128, k 512) = products 0 and 1
+    seams = {0: set(), 1: set(), 2: set()}
+    for members in ([2], [0, 1]):
+        N = sum(spec[i][1] for i in members)
+        for w in range(ncu):
+            r0, r1 = w * N // ncu, (w + 1) * N // ncu
+            for r in list(range(r0, r1, 256)) + [r1 - 1]:
+                for rr in (r - 1, r, r + 1, r + 255, r + 256):
+                    off = 0
+                    for i in members:
+                        if off <= rr < off + spec[i][1] and r0 <= rr < r1:
+                            seams[i].add(rr - off)
+                        off += spec[i][1]
+    for i, ((W, X, Y, _), (q, s, p, x, group, n, k)) in enumerate(zip(probs, refs)):
+        rows = np.array(sorted(set(range(0, n, 5)) | seams[i] | {n - 1}), dtype=np.int64)
+        pr = p.reshape(n, -1)[rows]
+        sr = s if group == 0 else s.reshape(n, -1)[rows]
+        yref = O.gemm(pr, 4, sr, group, len(rows), k, x, "bf16")
+        got = Y[:, torch.from_numpy(rows).to(DEV)].double().cpu().numpy()
+        check(got, yref, x, "bf16", q[rows], group, sr, f"m={m} product {i}")
+
+
 def test_mstream_plan_phase_chain():
     """phase 0: Y1 = W1 X0 (fp16 out, exact integers); phase 1: Y2 = W2 Y1."""
     m, k1, n1, n2 = 16, 1024, 2048, 700

@@ -436,13 +436,16 @@ __device__ __forceinline__ bool run_msegment(const StreamPhase& seg, const Strea
     cur = nx;
     return more;
   };
+  auto chunk = [&]<int H>() __attribute__((always_inline)) {
+    bool more = true;
+    [&]<int... T>(std::integer_sequence<int, T...>) __attribute__((always_inline)) {
+      ((more = more && step.template operator()<H, T>()), ...);
+    }(std::make_integer_sequence<int, TP>{});
+    return more;
+  };
   while (true) {
-    if (!step.template operator()<0, 0>()) break;
-    if constexpr (TP == 2)
-      if (!step.template operator()<0, 1>()) break;
-    if (!step.template operator()<1, 0>()) break;
-    if constexpr (TP == 2)
-      if (!step.template operator()<1, 1>()) break;
+    if (!chunk.template operator()<0>()) break;
+    if (!chunk.template operator()<1>()) break;
   }
   __syncthreads();  // LDS is reused by the next segment
   return true;
