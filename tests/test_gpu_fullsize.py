@@ -93,7 +93,7 @@ def split_rows(stack, order="independent"):
     else:
         ph = {"q": 0, "k": 0, "v": 0, "o": 1, "gate": 2, "up": 2, "down": 3}
         phases = {i: 4 * (i // per_layer) + ph[stack.shapes[i % per_layer][0]] for i in idx}
-    fmt = lambda i: (L[i][0].bits, L[i][0].group, L[i][0].zeros is not None, L[i][0].k)
+    fmt = lambda i: (L[i][0].bits, L[i][0].group, L[i][0].zeros is not None, -L[i][0].k)
     idx.sort(key=lambda i: (phases[i], fmt(i)))
     mfma = m >= 2 and all(W.bits == 4 and W.k % 512 == 0 for W, _, _ in L)
     segs = []

@@ -693,14 +693,17 @@ zq_status zq_plan_create(const zq_problem* problems, int count, int64_t m, zq_pl
     }
   }
   // Products of one phase do not depend on each other: order them by format
-  // (activation type, bit width, scale group, zero points, k), stably, so
-  // that each format of a phase is one segment. Few large segments keep every
-  // workgroup's load pipeline full; a segment boundary drains it.
+  // (activation type, bit width, scale group, zero points, then k from the
+  // longest rows down), stably, so that each format of a phase is one
+  // segment. Few large segments keep every workgroup's load pipeline full; a
+  // segment boundary drains it. Short rows last: a segment of short rows is
+  // bound by load latency, and starting the launch with it cost the
+  // tensor-parallel 7B share 2 % (K = 896 first: 5205 GB/s; last: 5311).
   std::vector<int> order(count);
   for (int i = 0; i < count; ++i) order[i] = i;
   auto fmt_key = [&](int i) {
     const zq_problem& q = problems[i];
-    return std::make_tuple(q.x_dtype, q.w.bits, q.w.group, q.w.zeros ? 1 : 0, q.w.k);
+    return std::make_tuple(q.x_dtype, q.w.bits, q.w.group, q.w.zeros ? 1 : 0, -q.w.k);
   };
   for (int a = 0; a < count;) {
     int b = a + 1;
