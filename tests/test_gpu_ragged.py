@@ -112,9 +112,10 @@ def test_partial_last_step_asymmetric(xdt, bits, m):
         check(Y.double().cpu().numpy(), ref(x, xdt), x, xdt, wdeq, what=f"n={n} k={k}")
 
 
+@pytest.mark.parametrize("xdt", ["f16", "bf16"])
 @pytest.mark.parametrize("bits", [2, 4, 8])
 @pytest.mark.parametrize("m", [1, 3])
-def test_partial_last_step_integer_inputs_bit_exact(bits, m):
+def test_partial_last_step_integer_inputs_bit_exact(xdt, bits, m):
     # integer activations, scales 0.5 / 1: every fp32 partial sum is exact, and
     # so is the zero padding of the partial step
     n, k = 90, 4736
@@ -123,10 +124,11 @@ def test_partial_last_step_integer_inputs_bit_exact(bits, m):
     s = np.where(g.random(n * k // 128) < 0.5, 0x3800, 0x3C00).astype(np.uint16)
     p = O.pack(q, bits)
     W = zq.ZqWeight(bits, 128, n, k, dev(p.reshape(-1)), dev(s.view(np.float16)))
-    x = g.integers(-4, 5, size=(m, k)).astype(np.float16)
-    Y = zq.gemm(W, x_dev(x, "f16"))
+    v = g.integers(-4, 5, size=(m, k)).astype(np.float32)
+    x = v.astype(np.float16) if xdt == "f16" else synth.f32_to_bf16_bits(v)
+    Y = zq.gemm(W, x_dev(x, xdt))
     torch.cuda.synchronize()
-    assert np.array_equal(Y.double().cpu().numpy(), O.gemm(p, bits, s, 128, n, k, x, "f16"))
+    assert np.array_equal(Y.double().cpu().numpy(), O.gemm(p, bits, s, 128, n, k, x, xdt))
 
 
 def test_activation_storage_past_k_is_never_read():
