@@ -8,6 +8,9 @@ namespace zq {
 bool mstream_supported(const void* packed, const uint16_t* scales, const uint16_t* zeros, int bits, int group,
                        int64_t m, int64_t k, const void* x, int64_t ldx) {
   if (bits != 4 || m < 2 || m > 32 || k <= 0 || k % MS_KC != 0) return false;
+  // buffer descriptors and 32-bit signed offsets: a 512-row block of codes
+  // and the m activation rows stay below 2 GB
+  if (2 * MS_HALF * (k / 2) >= ((int64_t)1 << 31) || m * ldx * 2 >= ((int64_t)1 << 31)) return false;
   if (((uintptr_t)packed & 15) || ((uintptr_t)x & 15) || ((ldx * 2) & 15)) return false;
   if (group && ((uintptr_t)scales & 7)) return false;
   if (zeros && (!group || ((uintptr_t)zeros & 7))) return false;
